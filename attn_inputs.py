@@ -1,0 +1,121 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module holds the workload shapes and the random-number recipe only; it
+does none of the attention arithmetic, so both the oracle and the HIP path
+may draw their inputs from it.
+
+Recipe: each tensor is drawn on the CPU with its own ``torch.Generator``
+seed as float32 ``randn`` (or ``rand`` - 0.5 for the uniform mix), scaled if
+the workload says so, then rounded once to fp16/bf16.  Both sides then read
+the same 16-bit values (the CPU reference consumes type-quantised inputs, as
+"Xe2 Sdp Bf16", section "Correctness Testing", prescribes).
+"""
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Lq: int
+    Lk: int
+    D: int
+    dtype: str  # "f16" | "bf16"
+    k_mult: float = 1.0
+    seed_base: int = 0
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def flops(self):
+        """Attention-forward FLOPs, 4*B*Hq*Lq*Lk*D (the two matrix products)."""
+        return 4 * self.B * self.Hq * self.Lq * self.Lk * self.D
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "f16" else torch.bfloat16
+
+    def describe(self):
+        return ("B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d %s%s" %
+                (self.B, self.Hq, self.Hkv, self.Lq, self.Lk, self.D, self.dtype,
+                 " K*%g" % self.k_mult if self.k_mult != 1.0 else ""))
+
+
+# The five workloads of the benchmark plan: the tiny case, the 4K and 8K
+# squares, the rectangular short-query/long-key case with sharpened softmax,
+# and the 16K x 16K, 32 Q / 2 KV head, HD=256 case (the shape of the
+# "Xe2 ... Flash Attention -- HD=256" page's headline figure).
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 1, 256, 256, 128, "f16", seed_base=1000),
+    "gqa4k_d256": Workload("gqa4k_d256", 1, 32, 2, 4096, 4096, 256, "f16", seed_base=2000),
+    "gqa8k_d128_bf16": Workload("gqa8k_d128_bf16", 1, 32, 8, 8192, 8192, 128, "bf16",
+                                seed_base=3000),
+    "rect1kx16k_d256": Workload("rect1kx16k_d256", 4, 32, 2, 1024, 16384, 256, "f16",
+                                k_mult=2.0, seed_base=4000),
+    "gqa16k_d256": Workload("gqa16k_d256", 1, 32, 2, 16384, 16384, 256, "f16",
+                            seed_base=5000),
+}
+HEADLINE = "gqa16k_d256"
+
+
+def _draw(shape, seed, dist):
+    g = torch.Generator().manual_seed(int(seed))
+    if dist == "normal":
+        return torch.randn(shape, generator=g, dtype=torch.float32)
+    if dist == "uniform":
+        return torch.rand(shape, generator=g, dtype=torch.float32) - 0.5
+    raise ValueError("unknown distribution %r" % dist)
+
+
+def make_qkv(B, Hq, Hkv, Lq, Lk, D, dtype="f16", seed=0, dist="normal", k_mult=1.0,
+             q_mult=1.0, v_mult=1.0):
+    """Q [B,Hq,Lq,D], K/V [B,Hkv,Lk,D] as CPU fp16/bf16 tensors.
+
+    Seeds: Q seed+1, K seed+2, V seed+3.
+    """
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    q = _draw((B, Hq, Lq, D), seed + 1, dist)
+    k = _draw((B, Hkv, Lk, D), seed + 2, dist)
+    v = _draw((B, Hkv, Lk, D), seed + 3, dist)
+    if q_mult != 1.0:
+        q = q * q_mult
+    if k_mult != 1.0:
+        k = k * k_mult
+    if v_mult != 1.0:
+        v = v * v_mult
+    return q.to(tdt), k.to(tdt), v.to(tdt)
+
+
+def workload_qkv(w: Workload):
+    return make_qkv(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, w.dtype, seed=w.seed_base,
+                    k_mult=w.k_mult)
+
+
+def sample_rows(w: Workload, n_random=1024, tile=128):
+    """Seeded subset of flat query rows (b*Hq + h)*Lq + i for large workloads.
+
+    n_random rows drawn without replacement (seed seed_base+4), plus every row
+    of the first and last ``tile``-row query tile of the first and last head,
+    plus rows 0 and Lq-1 of every head.  Sorted, unique.
+    """
+    total = w.B * w.Hq * w.Lq
+    rng = np.random.default_rng(w.seed_base + 4)
+    pick = [rng.choice(total, size=min(n_random, total), replace=False)]
+    first, last = 0, (w.B * w.Hq - 1) * w.Lq
+    t = min(tile, w.Lq)
+    pick.append(first + np.arange(t))
+    pick.append(first + w.Lq - t + np.arange(t))
+    pick.append(last + np.arange(t))
+    pick.append(last + w.Lq - t + np.arange(t))
+    heads = np.arange(w.B * w.Hq) * w.Lq
+    pick.append(heads)
+    pick.append(heads + w.Lq - 1)
+    return np.unique(np.concatenate(pick).astype(np.int64))

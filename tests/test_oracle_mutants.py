@@ -1,0 +1,58 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that the
+pins catch every one of them.
+
+Each mutant is the oracle's C source with one textual substitution, built
+with gcc into a temporary directory.  A mutant that passes every pin would
+mean the pins leave that part of the oracle unchecked.
+"""
+import os
+
+import pytest
+
+import oracle as oracle_pkg
+from oracle import build as oracle_build
+from oracle_pins import PINS
+
+SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "attn_oracle.c")
+
+MUTANTS = {
+    "drop_scale": ("e[j] = scale * dot;", "e[j] = dot;"),
+    "head_map_modulo": ("const int64_t g = h / G;", "const int64_t g = h % Hkv;"),
+    "no_max_subtraction": ("e[j] = exp(e[j] - m);", "e[j] = exp(e[j]); m = 0.0;"),
+    "lse_log2": ("*lse = m + log(sum);", "*lse = m + log2(sum);"),
+    "lse_without_max": ("*lse = m + log(sum);", "*lse = log(sum);"),
+    "transposed_k": ("dot += qrow[d] * kj[d];", "dot += qrow[d] * K[(d * Lk + j) % (Lk * D)];"),
+    "unnormalised_weights": ("const double p = e[j] / sum;", "const double p = e[j];"),
+    "last_key_dropped": ("for (int64_t j = 0; j < Lk; ++j) {\n    const double* kj",
+                         "for (int64_t j = 0; j < Lk - (Lk > 1); ++j) {\n    const double* kj"),
+    "value_row_index": ("const double* vj = V + j * D;", "const double* vj = V + ((j + 1) % Lk) * D;"),
+    "f16_exponent_bias": ("expo - 25", "expo - 24"),
+    "f16_subnormal_scale": ("(double)frac, -24", "(double)frac, -25"),
+    "bf16_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    "score_sign": ("e[j] = scale * dot;", "e[j] = -scale * dot;"),
+    "query_row_offset": ("qrow[d] = widen(q16[flat * D + d], dtype);",
+                         "qrow[d] = widen(q16[((flat + 1) % (B * Hq * Lq)) * D + d], dtype);"),
+}
+
+
+def _build_mutant(tmp_path, name):
+    before, after = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(before) >= 1, "mutation site for %s not found" % name
+    src = tmp_path / ("mutant_%s.c" % name)
+    src.write_text(text.replace(before, after, 1))
+    out = str(tmp_path / ("libmutant_%s.so" % name))
+    oracle_build.build(src=str(src), out=out, quiet=True)
+    return oracle_pkg.Oracle(out)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    orc = _build_mutant(tmp_path, name)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, "mutant %s passes every pin" % name
