@@ -1,0 +1,221 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step = one attention forward over the whole workload (every step of the method in the
+one kernel), inputs resident in HBM.  Prints ONE JSON line.  The default workload is the
+16K x 16K, 32 query / 2 key-value heads, HD=256, fp16 case; other names are listed in
+attn_inputs.WORKLOADS.
+
+The metric is attention TFLOPS = 4*B*Hq*Lq*Lk*D / time (the two matrix products) and its
+fraction of MI355X's dense fp16/bf16 MFMA peak.  The "Xe2 ... Flash Attention -- HD=256"
+page's formula (section "Performance Testing"), which adds 2*Lq*Lk*Hq for the softmax, is
+reported beside it.  The fp64 CPU oracle is timed on a seeded sample of query rows on the
+host cores (cpu_baseline) and checks the GPU output on those rows.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X dense fp16/bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU (AMD's 2.5 PFLOP/s).
+PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+METRIC = "attn fwd TFLOPS & % of MFMA peak, GQA 32Q/2KV HD=256 16Kx16K fp16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "flash_attention_amd", "csrc", f)
+                  for f in ("attn_fwd.hip", "attn_config.h")]
+
+
+def flops_headline(B, Hq, Lq, Lk, D):
+    return 4 * B * Hq * Lq * Lk * D
+
+
+def flops_pages(q_len, kv_len, hd, heads_q, batch=1):
+    """The pages' count: both matrix products plus 2 flops per score for the softmax."""
+    return batch * (4 * q_len * kv_len * hd * heads_q + 2 * q_len * kv_len * heads_q)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_sha") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def compare_rows(o_gpu, lse_gpu, rows, o_ref, lse_ref):
+    """Error metrics of the GPU output on the oracle's rows (NaN count first)."""
+    import numpy as np
+    import torch
+    idx = torch.from_numpy(np.asarray(rows, dtype=np.int64))
+    og = o_gpu.reshape(-1, o_gpu.shape[-1])[idx].double().numpy()
+    lg = lse_gpu.reshape(-1)[idx].double().numpy()
+    err = og - o_ref
+    return {"rows": int(len(rows)),
+            "nonfinite": int((~np.isfinite(og)).sum() + (~np.isfinite(lg)).sum()),
+            "rel_rms": float(np.sqrt((err ** 2).sum() / (o_ref ** 2).sum())),
+            "max_abs": float(np.abs(err).max()),
+            "lse_abs": float(np.abs(lg - lse_ref).max())}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--cpu-rows", type=int, default=6144,
+                    help="random query rows in the oracle sample")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import attn_inputs
+    import flash_attention_amd as fa
+
+    name = args.workload or attn_inputs.HEADLINE
+    w = attn_inputs.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    q, k, v = attn_inputs.workload_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device=dev)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    scale = float(np.float32(w.scale))
+    stream = torch.cuda.current_stream(dev)
+    code = fa.dtype_code(q)
+    plan = fa.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code)
+    args_c = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
+              w.Hq, w.Hkv, w.Lq, w.Lk, w.D, scale, code, stream.cuda_stream)
+    torch.cuda.synchronize()
+    print("[bench] %s inputs ready in %.1fs; plan %s grid=%d block_m=%d block_n=%d" %
+          (w.describe(), time.time() - t0, plan.kernel.decode(), plan.grid, plan.block_m,
+           plan.block_n), file=sys.stderr, flush=True)
+
+    def step():
+        rc = fa.attn_fwd_stream(*args_c)
+        if rc != 0:
+            raise fa.AttnError(rc, fa.attn_strerror(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    # Timed region: K steps, each bracketed by events on the launch stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    flops = flops_headline(w.B, w.Hq, w.Lq, w.Lk, w.D)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kern_avg = float(kms.mean())
+    achieved = flops / (kern_avg * 1e-3) / 1e12
+    print("[bench] kernel ms median %.4f min %.4f mean %.4f; wall/step %.4f ms" %
+          (np.median(kms), kms.min(), kern_avg, ms_per_step), file=sys.stderr, flush=True)
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: %d bytes read, %d bytes written" % (2 * n, 2 * n),
+              file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
+                   "Lk": w.Lk, "D": w.D, "in_dtype": w.dtype, "k_mult": w.k_mult,
+                   "scale": scale, "causal": False, "kernel": plan.kernel.decode(),
+                   "block_m": plan.block_m, "block_n": plan.block_n, "grid": plan.grid},
+        "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "kernel_ms": {"median": round(float(np.median(kms)), 4), "min": round(float(kms.min()), 4),
+                      "mean": round(kern_avg, 4)},
+        "tflops_pages_formula": round(flops_pages(w.Lq, w.Lk, w.D, w.Hq, w.B) /
+                                      (ms_per_step * 1e-3) / 1e12, 2),
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    traffic = measured_traffic(name)
+    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
+                       "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                       "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                       "algorithmic_flops_per_launch": flops}
+
+    if not args.no_cpu:
+        import oracle
+        rows = attn_inputs.sample_rows(w, n_random=min(args.cpu_rows, w.B * w.Hq * w.Lq))
+        threads = len(os.sched_getaffinity(0))
+        orc = oracle.default()
+        c0 = time.perf_counter()
+        o_ref, lse_ref = orc.attention(q, k, v, scale, rows=rows, nthreads=threads)
+        csec = time.perf_counter() - c0
+        cpu_flops = 4 * w.Lk * w.D * len(rows)
+        cm = compare_rows(o.cpu(), lse.cpu(), rows, o_ref, lse_ref)
+        out["cpu_baseline"] = {
+            "value": round(cpu_flops / csec / 1e12, 6), "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d query rows of this workload (seeded: %d random + first/last tiles "
+                      "and end rows of every head), fp64, %.1f s; extrapolated full oracle "
+                      "%.0f s" % (len(rows), min(args.cpu_rows, w.B * w.Hq * w.Lq), csec,
+                                  csec * w.B * w.Hq * w.Lq / len(rows))}
+        out["parity_on_sample"] = cm
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+"""GPU parity: the HIP kernels through the C ABI against the fp64 oracle, element by
+element, plus the invariants that hold exactly (or bitwise) on the GPU.
+
+Every case prints its name, shape and seed before it touches the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs
+import flash_attention_amd as fa
+import oracle
+from parity_util import check, gpu_fwd, metrics, parity, scale_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(what):
+    print("\n[case] %s" % what, flush=True)
+
+
+def _sweep():
+    shapes = [  # B, Hq, Hkv, Lq, Lk
+        (1, 2, 1, 128, 128), (1, 4, 1, 256, 256), (1, 2, 2, 512, 512), (1, 2, 1, 1024, 1024),
+        (1, 4, 2, 128, 1024), (1, 2, 1, 1024, 128), (1, 1, 1, 1, 1), (2, 4, 2, 17, 33),
+        (1, 2, 1, 129, 257), (1, 16, 1, 64, 200), (1, 8, 1, 100, 64), (2, 8, 4, 300, 190),
+    ]
+    dists = [("normal", 1.0), ("uniform", 1.0), ("normal", 4.0)]
+    cases = []
+    i = 0
+    for D in (128, 256):
+        for dt in ("f16", "bf16"):
+            for sh in shapes:
+                dist, km = dists[i % 3]
+                cases.append((*sh, D, dt, dist, km, 7000 + 10 * i))
+                i += 1
+    return cases
+
+
+SWEEP = _sweep()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=["B%d_H%d_%d_L%dx%d_D%d_%s_%s_k%g_s%d" % c
+                                             for c in SWEEP])
+def test_parity_sweep(case):
+    B, Hq, Hkv, Lq, Lk, D, dt, dist, km, seed = case
+    _announce(str(case))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, dt, seed=seed, dist=dist, k_mult=km)
+    parity(q, k, v, scale_of(D), dt, what=str(case))
+
+
+@pytest.mark.parametrize("name", list(attn_inputs.WORKLOADS))
+def test_parity_workload_full_size(name):
+    """The benchmark workloads at full size, in the launch the benchmark times; the
+    oracle checks a seeded subset of rows (all rows for the tiny case)."""
+    w = attn_inputs.WORKLOADS[name]
+    _announce("%s %s" % (name, w.describe()))
+    q, k, v = attn_inputs.workload_qkv(w)
+    rows = None if name == "tiny" else attn_inputs.sample_rows(w)
+    parity(q, k, v, w.scale, w.dtype, rows=rows, what=name)
+
+
+def test_worked_example_on_gpu():
+    """Two keys, D=256, scale 1/16: O = -tanh(1/2) in every coordinate, LSE = ln(1+e)."""
+    _announce("worked example")
+    D = 256
+    q = torch.zeros(1, 1, 1, D, dtype=torch.float16)
+    k = torch.zeros(1, 1, 2, D, dtype=torch.float16)
+    v = torch.empty(1, 1, 2, D, dtype=torch.float16)
+    q[..., 0] = 4.0
+    k[0, 0, 1, 0] = 4.0
+    v[0, 0, 0] = 1.0
+    v[0, 0, 1] = -1.0
+    o, lse = gpu_fwd(q, k, v, 1.0 / 16)
+    assert torch.allclose(o.double(), torch.full_like(o.double(), -math.tanh(0.5)), atol=1e-3)
+    assert abs(lse.item() - math.log1p(math.e)) <= 1e-5
+
+
+@pytest.mark.parametrize("D,dt", [(128, "f16"), (256, "bf16")])
+def test_single_key_is_exact(D, dt):
+    """Lk = 1: the weight is exactly 1, so O equals V_0 bit for bit."""
+    _announce("single key D=%d %s" % (D, dt))
+    q, k, v = attn_inputs.make_qkv(1, 4, 2, 77, 1, D, dt, seed=11)
+    o, lse = gpu_fwd(q, k, v, scale_of(D))
+    assert torch.equal(o, v.repeat_interleave(2, dim=1).expand(1, 4, 77, D))
+    s = (q.double() @ k.double().repeat_interleave(2, dim=1).transpose(-1, -2))[..., 0]
+    assert torch.allclose(lse.double(), s * float(np.float32(scale_of(D))), atol=1e-4)
+
+
+@pytest.mark.parametrize("D,dt", [(128, "bf16"), (256, "f16")])
+def test_gqa_equals_repeated_kv_bitwise(D, dt):
+    _announce("gqa vs repeated kv D=%d %s" % (D, dt))
+    q, k, v = attn_inputs.make_qkv(2, 8, 2, 200, 300, D, dt, seed=12)
+    o1, l1 = gpu_fwd(q, k, v, scale_of(D))
+    o2, l2 = gpu_fwd(q, k.repeat_interleave(4, dim=1).contiguous(),
+                     v.repeat_interleave(4, dim=1).contiguous(), scale_of(D))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("D,dt", [(128, "f16"), (256, "f16"), (256, "bf16")])
+def test_deterministic(D, dt):
+    """Two launches give bitwise equal results (an LDS race would show here)."""
+    _announce("determinism D=%d %s" % (D, dt))
+    q, k, v = attn_inputs.make_qkv(1, 8, 2, 1000, 1500, D, dt, seed=13)
+    o1, l1 = gpu_fwd(q, k, v, scale_of(D))
+    o2, l2 = gpu_fwd(q, k, v, scale_of(D))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_query_permutation_permutes_output_bitwise():
+    _announce("query permutation")
+    D = 256
+    q, k, v = attn_inputs.make_qkv(1, 2, 1, 384, 500, D, "f16", seed=14)
+    perm = torch.from_numpy(np.random.default_rng(14).permutation(384))
+    o1, l1 = gpu_fwd(q, k, v, scale_of(D))
+    o2, l2 = gpu_fwd(q[:, :, perm].contiguous(), k, v, scale_of(D))
+    assert torch.equal(o2, o1[:, :, perm]) and torch.equal(l2, l1[:, :, perm])
+
+
+def test_constant_values():
+    """Every value row equal to c: O = c up to the rounding of P to fp16."""
+    _announce("constant values")
+    D = 128
+    q, k, _ = attn_inputs.make_qkv(1, 4, 1, 300, 700, D, "f16", seed=15)
+    c = torch.linspace(-2, 2, D).to(torch.float16)
+    v = c.expand(1, 1, 700, D).contiguous()
+    o, _ = gpu_fwd(q, k, v, scale_of(D))
+    err = (o.double() - c.double()).abs().max().item()
+    assert err <= 4e-3, err
+
+
+def test_dominant_key():
+    """A key whose score exceeds all others by far selects its value row."""
+    _announce("dominant key")
+    D = 256
+    q, k, v = attn_inputs.make_qkv(1, 2, 1, 64, 300, D, "f16", seed=16)
+    k[0, 0, 123] = q[0, 0, 0] * 8  # row 0 of head 0: score ~ 8*|q|^2/16 >> others
+    o, _ = gpu_fwd(q, k, v, scale_of(D))
+    o_ref, lse_ref = oracle.attention(q, k, v, float(np.float32(scale_of(D))), rows=[0])
+    assert torch.allclose(o[0, 0, 0].double(), torch.from_numpy(o_ref[0]), atol=2e-3)
+    assert torch.allclose(o[0, 0, 0].double(), v[0, 0, 123].double(), atol=2e-3)
+
+
+def test_lse_optional_and_output_unchanged():
+    _announce("lse NULL")
+    D = 128
+    q, k, v = attn_inputs.make_qkv(1, 4, 2, 200, 200, D, "bf16", seed=17)
+    o1, _ = gpu_fwd(q, k, v, scale_of(D), with_lse=True)
+    o2, _ = gpu_fwd(q, k, v, scale_of(D), with_lse=False)
+    assert torch.equal(o1, o2)
+
+
+def test_null_stream_entry_point():
+    """attn_fwd (null stream) and attn_fwd_stream give the same bits."""
+    _announce("attn_fwd null stream")
+    D = 256
+    q, k, v = attn_inputs.make_qkv(1, 2, 1, 130, 70, D, "f16", seed=18)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=dev)
+    torch.cuda.synchronize()
+    rc = fa.attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     1, 2, 1, 130, 70, D, 1 / 16, fa.ATTN_F16)
+    assert rc == 0
+    torch.cuda.synchronize()
+    o2, l2 = gpu_fwd(q, k, v, 1 / 16)
+    assert torch.equal(o.cpu(), o2) and torch.equal(lse.cpu(), l2)
+
+
+def test_rejected_call_writes_nothing():
+    _announce("rejected call")
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 2, 64, 64, device=dev).half()
+    o = torch.full_like(q, float("nan"))
+    torch.cuda.synchronize()
+    rc = fa.attn_fwd_stream(q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), None,
+                            1, 2, 2, 64, 64, 64, 0.125, fa.ATTN_F16,
+                            torch.cuda.current_stream().cuda_stream)
+    assert rc == -3
+    torch.cuda.synchronize()
+    assert torch.isnan(o.float()).all()
+
+
+def test_scale_sign_and_zero():
+    """Negative and zero scales follow the definition (zero: O = mean of V)."""
+    _announce("scale sign/zero")
+    D = 128
+    q, k, v = attn_inputs.make_qkv(1, 2, 1, 96, 160, D, "f16", seed=19)
+    parity(q, k, v, -0.2, "f16", what="scale=-0.2")
+    o, lse = gpu_fwd(q, k, v, 0.0)
+    mean = v.double().mean(dim=2, keepdim=True)
+    assert (o.double() - mean).abs().max().item() <= 2e-3
+    assert (lse.double() - math.log(160)).abs().max().item() <= 1e-5
