@@ -2,9 +2,8 @@
 // of the C ABI.
 //
 // Method: the flash-attention forward of the "Xe2 (Lunar Lake/LNL, Battlemage/BMG) ESIMD
-// Flash Attention -- HD=256" page (GQA, online softmax over key tiles, deferred rescale of
-// the output accumulator, one reciprocal of the row sum at the end: sections "Key
-// Optimization Insights / What Worked") with the fp32-softmax data flow of "Xe2 Sdp Bf16"
+// Flash Attention -- HD=256" page (GQA, online softmax over key tiles, one reciprocal of
+// the row sum at the end: sections "Key Optimization Insights / What Worked") with the fp32-softmax data flow of "Xe2 Sdp Bf16"
 // (section "Kernel Architecture: bf16io", data-flow diagram).  The Xe2 register and SLM
 // choreography is not reused; the layout below is built around CDNA4's 32x32x16 MFMA.
 //
@@ -20,17 +19,21 @@
 // max = an in-lane max plus one cross-half exchange; the row sum stays per-lane until the
 // end.  Those same registers, rounded to 16 bits, are directly the B operand of
 // O^T += V^T * P^T (k index = key): no trip through LDS for P.  The key order inside the
-// B operand is fixed by the accumulator layout, so V^T is stored in LDS in that same
-// permuted key order (see vt_pos_group).  O^T lives in 32x32 accumulators with one query
-// per lane column as well, so the per-row rescale by alpha is a per-lane scalar multiply.
+// B operand is fixed by the accumulator layout, so V^T must be read in that same
+// key order, which the transposing LDS reads of V provide.  O^T lives in 32x32 accumulators
+// with one query per lane column as well.
 //
-// This is the first, correctness-first version: K and V tiles are staged through registers
-// into a single LDS buffer, two barriers per tile.
+// Pipeline.  K and V tiles of 32 keys are copied straight from HBM into LDS (no register
+// staging), three tiles resident: tile t+2 is in flight while tile t is consumed, with one
+// workgroup barrier per tile.  Each wavefront owns 64 query rows (two 32-row MFMA blocks),
+// so every K and V fragment read from LDS feeds two MFMAs; Q stays in registers and the
+// output accumulator in AGPRs for the whole key loop.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "../../include/attn.h"
+#include "attn_agpr.h"
 #include "attn_config.h"
 
 namespace {
@@ -55,14 +58,32 @@ struct Params {
   float c;  // scale * log2(e): scores are kept in base-2 units
 };
 
+// 32x32x16 MFMA issued through inline asm.  The score accumulator is pinned to VGPRs ("v":
+// the softmax reads it with VALU instructions); the output accumulator lives in fixed AGPRs
+// (attn_agpr.h), written only by MFMAs inside the key loop.  The compiler does not look for
+// hazards inside inline asm, so the statements carry their own wait states: 3 before each
+// MFMA (a source may have been written by the VALU instruction just before; the ISA asks
+// for 2), and every reader of an MFMA result is ordered behind a fence of 24 wait states
+// (an 8-pass XDL result needs NumPasses + 3 before a VALU read).
+#define ATTN_MFMA_F16 "v_mfma_f32_32x32x16_f16"
+#define ATTN_MFMA_BF16 "v_mfma_f32_32x32x16_bf16"
+#define ATTN_MFMA_STMTS(OPC)                                                              \
+  static __device__ __forceinline__ void mfma_v0(u32x4 a, u32x4 b, f32x16& c) {           \
+    asm volatile("s_nop 2\n\t" OPC " %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));          \
+  }                                                                                       \
+  static __device__ __forceinline__ void mfma_v(u32x4 a, u32x4 b, f32x16& c) {            \
+    asm volatile("s_nop 2\n\t" OPC " %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));          \
+  }
+
 template <typename T>
 struct Elt;
 
 template <>
 struct Elt<_Float16> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  ATTN_MFMA_STMTS(ATTN_MFMA_F16)
+  // output accumulator block n += a * b (block n: AGPRs 16n..16n+15)
+  static __device__ __forceinline__ void acc_mfma(int n, u32x4 a, u32x4 b) {
+    attn_agpr::mfma_f16(n, a, b);
   }
   // two fp32 -> two fp16, round to nearest even
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
@@ -73,9 +94,9 @@ struct Elt<_Float16> {
 
 template <>
 struct Elt<__bf16> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  ATTN_MFMA_STMTS(ATTN_MFMA_BF16)
+  static __device__ __forceinline__ void acc_mfma(int n, u32x4 a, u32x4 b) {
+    attn_agpr::mfma_bf16(n, a, b);
   }
   static __device__ __forceinline__ uint32_t pack2(float x, float y) {
     bf16x2 r = __builtin_convertvector((f32x2){x, y}, bf16x2);
@@ -83,33 +104,89 @@ struct Elt<__bf16> {
   }
 };
 
-// The S^T accumulator register r of a lane in half h (= lane/32) holds key
-// 8*(r/4) + 4*h + r%4 of its 32-key block.  The P^T operand of MFMA step ks (16 keys) takes
-// registers 8*(ks%2) .. +7, i.e. key groups (of 4) 4ks+h and 4ks+2+h for lane half h.  V^T
-// is therefore stored with key group kg at position group vt_pos_group(kg): the two middle
-// groups of every 4 swap places, so lane half h reads its 8 keys as one 16-byte run.
-__device__ __forceinline__ int vt_pos_group(int kg) {
-  return (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1);
+// Wait states between the last MFMA writing x and any other use of x (see above).
+__device__ __forceinline__ void mfma_fence_v(f32x16& x) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
-template <int D, typename T>
+// ---------------------------------------------------------------------------------------
+// LDS layouts.  K and V tiles are stored row-major [key][d] exactly as in HBM, except that
+// the 16-byte chunks of each row are XOR-permuted so the fragment reads are bank-conflict
+// free; the permutation is applied on the global side of the direct global->LDS copy
+// (lane i of a wave always lands at LDS base + 16*i, so each lane fetches the chunk that
+// belongs at its slot).
+//   K: chunk c of row r sits at slot c ^ (r & 7).  The S^T A-operand read has lanes
+//      0..7 on rows 0..7 at one chunk: eight distinct 16-byte bank groups.
+//   V: chunk c of row r sits at slot c ^ 2*(r & 3).  A transposing read of 16 lanes covers
+//      4 consecutive rows x 32 bytes; the XOR spreads the 4 row segments over 8 distinct
+//      16-byte bank groups.
+__device__ __forceinline__ int swz_k(int r) { return r & 7; }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+// Direct global->LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane i's
+// bytes land at LDS address dst + 16*i (dst wave-uniform, passed in M0).  The source is a
+// buffer resource (base, size in bytes) plus a per-lane byte offset: offsets at or past the
+// size read as zero, which is how rows past the end of K and V are filled.  Written as
+// inline asm so that the compiler does not add its own conservative vmcnt waits before every
+// LDS read in the loop; completion is tracked by hand with WAIT_VMCNT + a workgroup
+// barrier.  M0 is used by nothing else in these kernels.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uintptr_t>(base);
+  // dword3: 32-bit data format, no swizzle, raw (stride 0) addressing.  The descriptor must
+  // sit in SGPRs: every field is wave-uniform, readfirstlane says so to the compiler.
+  return (i32x4){__builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu)),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)),
+                 __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
+}
+
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, const uint16_t* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)dst)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+// Growth threshold, log2 units.  The exponentials use a per-row reference m fixed by the
+// first key tile; a later score may exceed m by up to kTau, so weights stay below 2^15 (fp16
+// holds up to 65504).  Exact in real arithmetic: numerator and denominator share m.
+constexpr float kTau = 15.0f;
+
+template <int D, typename T, bool NEG>
 __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params p) {
   constexpr int QB = attn_cfg::Tile<D>::QB;
   constexpr int BN = attn_cfg::Tile<D>::BN;
-  constexpr int NB = BN / 32;   // 32-key blocks per tile
+  constexpr int NSTAGE = attn_cfg::Tile<D>::STAGES;
+  static_assert(BN == 32, "one 32-key MFMA block per tile");
   constexpr int KS = D / 16;    // contraction steps of S^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
-  constexpr int KROW = D + attn_cfg::kPad;
-  constexpr int VROW = BN + attn_cfg::kPad;
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int TILE = BN * D;  // elements of one K (or V) tile
+  constexpr int LOADS = BN * CPR / attn_cfg::kThreads;  // 16-byte copies per thread per tile
   constexpr int BM = attn_cfg::block_m(QB);
-  constexpr int NT = attn_cfg::kThreads;
+  // NEG: scale < 0, so the largest scaled score comes from the smallest raw score.
+  constexpr float kWorst = NEG ? __builtin_inff() : -__builtin_inff();
 
   extern __shared__ u32x4 smem_raw[];
-  uint16_t* ks = reinterpret_cast<uint16_t*>(smem_raw);
-  uint16_t* vt = ks + BN * KROW;
+  uint16_t* const smem = reinterpret_cast<uint16_t*>(smem_raw);
+  // Two restart flags after the K/V stages (written by at most one lane per wave).
+  volatile int* const restart_flag = reinterpret_cast<volatile int*>(smem + NSTAGE * 2 * TILE);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber so each XCD runs a contiguous
@@ -129,173 +206,252 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const uint16_t* vh = p.v + ((size_t)b * p.Hkv + hkv) * p.Lk * D;
   const int qrow0 = qtile * BM + wave * 32 * QB;
   const int Lk = p.Lk;
+  const int ntiles = (Lk + BN - 1) / BN;
+  const int nfull = Lk / BN;  // tiles whose 32 keys are all valid; tile nfull is partial
 
-  // Q^T operand fragments, resident for the whole key loop: lane l holds query row l%32,
-  // dims 16*kk + 8*(l/32) .. +7.
+  // Direct global->LDS copy of K and V tile t into stage st.  Each thread copies LOADS
+  // 16-byte chunks of each; its byte offsets inside a tile never change, the tile start goes
+  // into the buffer base.  Rows past Lk fall outside the buffer and read as zeros (their
+  // scores are masked, their weights are zero).
+  uint32_t voff_k[LOADS], voff_v[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = i * attn_cfg::kThreads + wave * 64 + lane;
+    const int r = pos / CPR, c = pos % CPR;
+    voff_k[i] = static_cast<uint32_t>(r * D * 2 + (c ^ swz_k(r)) * 16);
+    voff_v[i] = static_cast<uint32_t>(r * D * 2 + (c ^ swz_v(r)) * 16);
+  }
+  const uint32_t kv_bytes = static_cast<uint32_t>(Lk) * D * 2;
+  auto issue_tile = [&](int t, int st) {
+    uint16_t* ks = smem + st * 2 * TILE;
+    uint16_t* vs = ks + TILE;
+    const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // bytes before tile t
+    const i32x4 rk = make_rsrc(kh + (size_t)t * TILE, kv_bytes - skip);
+    const i32x4 rv = make_rsrc(vh + (size_t)t * TILE, kv_bytes - skip);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int slot0 = i * attn_cfg::kThreads + wave * 64;  // wave-uniform first slot
+      lds_dma16(rk, voff_k[i], ks + slot0 * 8);
+      lds_dma16(rv, voff_v[i], vs + slot0 * 8);
+    }
+  };
+
+  // Q^T operand fragments, register resident for the whole key loop: lane l holds query
+  // row l%32 of block qb, dims 16*kk + 8*(l/32) .. +7.  Rows past Lq re-read row Lq-1
+  // (never stored).
   u32x4 qf[QB][KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = qrow0 + qb * 32 + l32;
+    const int row = min(qrow0 + qb * 32 + l32, p.Lq - 1);
     const u32x4* src = reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 8 * hi);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = row < p.Lq ? src[2 * kk] : (u32x4){0, 0, 0, 0};
+    for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = src[2 * kk];
   }
 
-  f32x16 acc[QB][DB];
+  issue_tile(0, 0);
+  if (ntiles > 1) issue_tile(1, 1);
+  if (tid < 2) restart_flag[tid] = 0;  // 0 never matches an iteration number (read at it >= 1)
+
+  // Per-lane LDS element offsets of the fragment reads (stage base added later).
+  // K (A operand of S^T): row l%32, chunk 2kk+hi, permuted; kk = 4g+u splits into a
+  // lane-dependent part (u) and an immediate (64*g elements).
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = l32 * D + (((2 * u + hi) ^ swz_k(l32)) * 8);
+  // V^T (A operand of O^T) through ds_read_b64_tr_b16: in each 16-lane block, source lane
+  // 4e+c supplies row (key) e, 4 dims at 4c of the block's 16 dims; lane i then receives
+  // dim i of those 4 rows.  Lane block b16 = lane/16: half h = b16/2 selects keys 4h..4h+3
+  // (of each group of 8), b16%2 selects dims 16..31 of the 32-dim block.
+  int voff[2];
+  {
+    const int b16 = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
+    const int h = b16 >> 1, dh = b16 & 1;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int chunk = 4 * par + 2 * dh + (c >> 1);
+      voff[par] = (4 * h + e) * D + ((chunk ^ swz_v(4 * h + e)) * 8) + (c & 1) * 4;
+    }
+  }
+
+  // Output accumulator O^T, block (qb, db) = AGPR block qb*DB + db (attn_agpr.h).
   float m[QB], l[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -__builtin_inff();
     l[qb] = 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc[qb][db] = (f32x16){};
+    for (int db = 0; db < DB; ++db) attn_agpr::zero(qb * DB + db);
   }
+  const float c = p.c;
 
-  const int ntiles = (Lk + BN - 1) / BN;
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * BN;
-    __syncthreads();  // every wave is done reading the previous tile
-    // K tile, row-major [key][d], coalesced 16-byte loads.
-#pragma unroll
-    for (int it = 0; it < BN * D / 8 / NT; ++it) {
-      const int id = tid + it * NT;
-      const int key = id / (D / 8), c = id % (D / 8);
-      u32x4 val = {0, 0, 0, 0};
-      if (j0 + key < Lk) val = *reinterpret_cast<const u32x4*>(kh + (size_t)(j0 + key) * D + c * 8);
-      *reinterpret_cast<u32x4*>(ks + key * KROW + c * 8) = val;
-    }
-    // V tile, transposed to [d][key position]: each thread takes 4 keys x 8 dims.
-#pragma unroll
-    for (int it = 0; it < (BN / 4) * (D / 8) / NT; ++it) {
-      const int id = tid + it * NT;
-      const int kg = id / (D / 8), c = id % (D / 8);
-      u32x4 r[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = j0 + kg * 4 + e;
-        r[e] = key < Lk ? *reinterpret_cast<const u32x4*>(vh + (size_t)key * D + c * 8)
-                        : (u32x4){0, 0, 0, 0};
-      }
-      const int pg = vt_pos_group(kg);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int sh = 16 * (i & 1);
-        const uint32_t e0 = (r[0][i >> 1] >> sh) & 0xffffu, e1 = (r[1][i >> 1] >> sh) & 0xffffu;
-        const uint32_t e2 = (r[2][i >> 1] >> sh) & 0xffffu, e3 = (r[3][i >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2*>(vt + (c * 8 + i) * VROW + pg * 4) =
-            (u32x2){e0 | (e1 << 16), e2 | (e3 << 16)};
-      }
-    }
-    __syncthreads();
-
-    // S^T = K * Q^T, fp32 accumulation.
-    f32x16 s[NB][QB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[nb][qb] = (f32x16){};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(ks + (nb * 32 + l32) * KROW + kk * 16 + 8 * hi);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[nb][qb] = Elt<T>::mfma(a, qf[qb][kk], s[nb][qb]);
-      }
-    }
-
-    // Online softmax in base 2 (fp32).  Keys past Lk get -inf.
-    const bool tail = j0 + BN > Lk;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[nb][qb][r] * p.c;
-          if (tail) {
-            const int key = j0 + nb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= Lk) x = -__builtin_inff();
-          }
-          s[nb][qb][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-      float sum = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(s[nb][qb][r] - mnew);
-          s[nb][qb][r] = e;
-          sum += e;
-        }
-      }
-      l[qb] = l[qb] * alpha + sum;
-      m[qb] = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-    }
-
-    // O^T += V^T * P^T, P rounded to the input type in registers.
-#pragma unroll
-    for (int ks16 = 0; ks16 < BN / 16; ++ks16) {
-      const int nb = ks16 >> 1, half = ks16 & 1;
-      u32x4 pb[QB];
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  // The key loop.  `it` counts iterations including restarts (see below) and never resets,
+  // so the restart flags written in one iteration cannot be mistaken for another's.
+  int t = 0;
+  for (int it = 0;; ++it) {
+    // Tile t was issued two iterations ago (or in the prologue); only tile t+1 may still be
+    // in flight, so wait for all but this thread's copies of tile t+1.
+    if (t + 1 < ntiles) WAIT_VMCNT(2 * LOADS);
+    else WAIT_VMCNT(0);
+    __syncthreads();  // everyone's share of tile t landed; stage of tile t-1 is free
+    // Restart.  A wave whose row maximum outgrew its reference m by more than kTau in the
+    // previous iteration raised m and flagged it; every wave then starts the key sweep over
+    // with zeroed accumulators (the waves' references stay valid).  This replaces the usual
+    // per-tile rescale of the output accumulator by alpha = exp2(m_old - m_new): the
+    // accumulator is only ever written by MFMAs, and with the first tile fixing m the
+    // restart is rare (the scores must grow by more than 2^kTau over the first tile's).
+    if (it > 0 && __builtin_amdgcn_readfirstlane(restart_flag[(it - 1) & 1]) == it) {
+      WAIT_VMCNT(0);
+      __syncthreads();  // nobody still reads a stage
+      issue_tile(0, 0);
+      if (ntiles > 1) issue_tile(1, 1);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const f32x16& sv = s[nb][qb];
-        pb[qb] = (u32x4){Elt<T>::pack2(sv[8 * half + 0], sv[8 * half + 1]),
-                         Elt<T>::pack2(sv[8 * half + 2], sv[8 * half + 3]),
-                         Elt<T>::pack2(sv[8 * half + 4], sv[8 * half + 5]),
-                         Elt<T>::pack2(sv[8 * half + 6], sv[8 * half + 7])};
+        l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) attn_agpr::zero(qb * DB + db);
       }
+      t = 0;
+      continue;
+    }
+    if (t >= ntiles) break;
+    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
+    const uint16_t* ks = smem + (t % NSTAGE) * 2 * TILE;
+    const uint16_t* vs = ks + TILE;
+
+    // ---- S^T = K Q^T (fp32 accumulation) ----
+    f32x16 sacc[QB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(vt + (db * 32 + l32) * VROW + ks16 * 16 + 8 * hi);
+    for (int kk = 0; kk < KS; ++kk) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ks + koff[kk & 3] + (kk >> 2) * 64);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = Elt<T>::mfma(a, pb[qb], acc[qb][db]);
+      for (int qb = 0; qb < QB; ++qb) {
+        if (kk == 0) Elt<T>::mfma_v0(a, qf[qb][kk], sacc[qb]);
+        else Elt<T>::mfma_v(a, qf[qb][kk], sacc[qb]);
       }
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mfma_fence_v(sacc[qb]);
+    // Keys past Lk (last tile only): the score becomes the worst value, so the key drops out
+    // of the maximum and its weight exp2(c*score - m) is exactly 0.  Accumulator register r
+    // of this lane holds key t*BN + 8*(r/4) + 4*hi + r%4.
+    if (t == nfull) {
+      const int kvalid = Lk - t * BN - 4 * hi;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) >= kvalid) sacc[qb][r] = kWorst;
+    }
+
+    // ---- online softmax (fp32, base 2) ----
+    float mt[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float x = kWorst;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x = NEG ? fminf(x, sacc[qb][r]) : fmaxf(x, sacc[qb][r]);
+      }
+      const float y = __shfl_xor(x, 32);
+      x = NEG ? fminf(x, y) : fmaxf(x, y);
+      mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
+    }
+    if (t == 0) {
+      // Nothing accumulated yet: the first tile just sets the reference.
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m[qb] = fmaxf(m[qb], mt[qb]);
+    } else {
+      bool grow = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        grow |= mt[qb] > m[qb] + kTau;
+        m[qb] = mt[qb] > m[qb] + kTau ? mt[qb] : m[qb];
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0 && lane == 0) restart_flag[it & 1] = it + 1;
+    }
+    u32x4 pb[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mneg = -m[qb];
+      float pv[16];
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, mneg));
+        pv[r] = e;
+        sum += e;
+      }
+      l[qb] += sum;
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8)
+        pb[qb][h8] = (u32x4){Elt<T>::pack2(pv[8 * h8 + 0], pv[8 * h8 + 1]),
+                             Elt<T>::pack2(pv[8 * h8 + 2], pv[8 * h8 + 3]),
+                             Elt<T>::pack2(pv[8 * h8 + 4], pv[8 * h8 + 5]),
+                             Elt<T>::pack2(pv[8 * h8 + 6], pv[8 * h8 + 7])};
+    }
+
+    // ---- O^T += V^T P^T ----
+    // MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator registers
+    // 8ks..8ks+7, whose keys for lane half h are 16ks + {4h..4h+3, 8+4h..8+4h+3}: the two
+    // transposing reads (rows +0 and +8) fetch exactly those rows of V.
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int ks16 = 0; ks16 < 2; ++ks16) {
+        const uint16_t* base = vs + voff[db & 1] + (db >> 1) * 64 + 16 * ks16 * D;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * D));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+        const u32x4 a = {lo2[0], lo2[1], up2[0], up2[1]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) Elt<T>::acc_mfma(qb * DB + db, a, pb[qb][ks16]);
+      }
+    }
+    ++t;
   }
 
   // Epilogue: O = O^T / l (one reciprocal per row), LSE = ln2 * (m + log2 l).
+  attn_agpr::fence();
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l[qb] + __shfl_xor(l[qb], 32);
     const float inv = 1.0f / lt;
     const int row = qrow0 + qb * 32 + l32;
-    if (row < p.Lq) {
-      uint16_t* dst = p.o + ((size_t)bh * p.Lq + row) * D + 4 * hi;
+    uint16_t* dst = p.o + ((size_t)bh * p.Lq + min(row, p.Lq - 1)) * D + 4 * hi;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db) {
+      float x[16];
+      attn_agpr::read4<0>(qb * DB + db, x[0], x[1], x[2], x[3]);
+      attn_agpr::read4<1>(qb * DB + db, x[4], x[5], x[6], x[7]);
+      attn_agpr::read4<2>(qb * DB + db, x[8], x[9], x[10], x[11]);
+      attn_agpr::read4<3>(qb * DB + db, x[12], x[13], x[14], x[15]);
+      if (row < p.Lq) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x16& a = acc[qb][db];
-          const u32x2 w = {Elt<T>::pack2(a[4 * g] * inv, a[4 * g + 1] * inv),
-                           Elt<T>::pack2(a[4 * g + 2] * inv, a[4 * g + 3] * inv)};
+          const u32x2 w = {Elt<T>::pack2(x[4 * g] * inv, x[4 * g + 1] * inv),
+                           Elt<T>::pack2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
           *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * g) = w;
         }
       }
-      if (p.lse && hi == 0)
-        p.lse[(size_t)bh * p.Lq + row] = (m[qb] + __builtin_log2f(lt)) * 0.69314718055994531f;
     }
+    if (p.lse && hi == 0 && row < p.Lq)
+      p.lse[(size_t)bh * p.Lq + row] = (m[qb] + __builtin_log2f(lt)) * 0.69314718055994531f;
   }
 }
 
 template <int D, typename T>
 int launch(const Params& prm, int64_t grid, hipStream_t stream) {
-  constexpr int lds = attn_cfg::lds_bytes(D, attn_cfg::Tile<D>::BN);
+  constexpr int lds =
+      attn_cfg::lds_bytes(D, attn_cfg::Tile<D>::BN, attn_cfg::Tile<D>::STAGES);
   static_assert(lds <= 160 * 1024, "LDS budget of one CU exceeded");
-  const void* fn = reinterpret_cast<const void*>(&attn_fwd_kernel<D, T>);
-  static const hipError_t attr =
-      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const void* fn = prm.c < 0.f ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, true>)
+                               : reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, false>);
+  static const hipError_t attr[2] = {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds)};
   (void)attr;
   Params local = prm;
   void* args[] = {&local};
@@ -328,6 +484,11 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   prm.Lk = static_cast<int>(Lk);
   prm.n_qtiles = static_cast<int>((Lq + plan.block_m - 1) / plan.block_m);
   prm.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  // scale == 0: every weight is 1.  A positive c this small gives c*score below 2^-60 for
+  // any finite fp16/bf16 dot product, so exp2 rounds to exactly 1 and the LSE term c*m
+  // vanishes against ln(Lk) -- the same fp32 results, while masked keys (score -inf) still
+  // get weight exp2(-inf) = 0 instead of exp2(0 * -inf) = NaN.
+  if (prm.c == 0.f) prm.c = 1e-30f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (D == 128)
     return in_dtype == ATTN_F16 ? launch<128, _Float16>(prm, plan.grid, s)

@@ -20,7 +20,7 @@ bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
 }
 
 struct PlanInternal {
-  int qb, bn, block_m, lds;
+  int qb, bn, stages, block_m, lds;
 };
 
 bool plan_for_d(int64_t D, PlanInternal* p) {
@@ -28,14 +28,16 @@ bool plan_for_d(int64_t D, PlanInternal* p) {
   if (D == 128) {
     p->qb = Tile<128>::QB;
     p->bn = Tile<128>::BN;
+    p->stages = Tile<128>::STAGES;
   } else if (D == 256) {
     p->qb = Tile<256>::QB;
     p->bn = Tile<256>::BN;
+    p->stages = Tile<256>::STAGES;
   } else {
     return false;
   }
   p->block_m = block_m(p->qb);
-  p->lds = lds_bytes(static_cast<int>(D), p->bn);
+  p->lds = lds_bytes(static_cast<int>(D), p->bn, p->stages);
   return true;
 }
 
