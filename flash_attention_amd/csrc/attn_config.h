@@ -18,14 +18,14 @@ template <>
 struct Tile<128> {
   static constexpr int QB = 2;      // 32-row query blocks per wavefront
   static constexpr int BN = 32;     // keys per LDS tile
-  static constexpr int STAGES = 3;  // K/V tiles resident in LDS at once
+  static constexpr int STAGES = 4;  // K/V tiles resident in LDS at once
 };
 
 template <>
 struct Tile<256> {
   static constexpr int QB = 2;
   static constexpr int BN = 32;
-  static constexpr int STAGES = 3;
+  static constexpr int STAGES = 4;
 };
 
 constexpr int block_m(int qb) { return kWaves * 32 * qb; }

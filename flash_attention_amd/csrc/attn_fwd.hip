@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/attn.h"
 #include "attn_agpr.h"
@@ -115,13 +116,14 @@ __device__ __forceinline__ void mfma_fence_v(f32x16& x) {
 // free; the permutation is applied on the global side of the direct global->LDS copy
 // (lane i of a wave always lands at LDS base + 16*i, so each lane fetches the chunk that
 // belongs at its slot).
-//   K: chunk c of row r sits at slot c ^ (r & 7).  The S^T A-operand read has lanes
-//      0..7 on rows 0..7 at one chunk: eight distinct 16-byte bank groups.
-//   V: chunk c of row r sits at slot c ^ 2*(r & 3).  A transposing read of 16 lanes covers
-//      4 consecutive rows x 32 bytes; the XOR spreads the 4 row segments over 8 distinct
-//      16-byte bank groups.
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+//   K: chunk c of row r sits at slot c ^ (r & 15).  The S^T A-operand read (ds_read_b128)
+//      serves 16 lanes per LDS cycle, here rows 0..15 (or 16..31) at one chunk: sixteen
+//      distinct 16-byte slots, all 64 banks.
+//   V: chunk c of row r sits at slot c ^ 4*(r & 3).  A transposing read (ds_read_b64_tr_b16)
+//      serves 32 lanes per cycle: 4 consecutive rows x 64 bytes, which the XOR moves to 4
+//      distinct 64-byte bank groups.
+__device__ __forceinline__ int swz_k(int r) { return r & 15; }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -169,13 +171,16 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   constexpr int QB = attn_cfg::Tile<D>::QB;
   constexpr int BN = attn_cfg::Tile<D>::BN;
   constexpr int NSTAGE = attn_cfg::Tile<D>::STAGES;
-  static_assert(BN == 32, "one 32-key MFMA block per tile");
+  static_assert(BN == 32 && QB == 2, "two 32-row query blocks, one 32-key block per tile");
+  static_assert(NSTAGE == 4, "tiles t-1 (V), t (K), t+1, t+2 (in flight) resident");
   constexpr int KS = D / 16;    // contraction steps of S^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int TILE = BN * D;  // elements of one K (or V) tile
-  constexpr int LOADS = BN * CPR / attn_cfg::kThreads;  // 16-byte copies per thread per tile
+  constexpr int LOADS = BN * CPR / attn_cfg::kThreads;     // 16-byte copies per thread per tile
+  constexpr int ROWS_PER_LOAD = attn_cfg::kThreads / CPR;  // tile rows one copy round covers
   constexpr int BM = attn_cfg::block_m(QB);
+  constexpr int NSTEP = 2 * DB;  // P.V steps per tile, two MFMAs (one per query block) each
   // NEG: scale < 0, so the largest scaled score comes from the smallest raw score.
   constexpr float kWorst = NEG ? __builtin_inff() : -__builtin_inff();
 
@@ -209,30 +214,34 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const int ntiles = (Lk + BN - 1) / BN;
   const int nfull = Lk / BN;  // tiles whose 32 keys are all valid; tile nfull is partial
 
-  // Direct global->LDS copy of K and V tile t into stage st.  Each thread copies LOADS
-  // 16-byte chunks of each; its byte offsets inside a tile never change, the tile start goes
-  // into the buffer base.  Rows past Lk fall outside the buffer and read as zeros (their
-  // scores are masked, their weights are zero).
-  uint32_t voff_k[LOADS], voff_v[LOADS];
+  // ---- direct HBM->LDS copies of K and V tiles ----
+  // Copy round i of this thread moves tile row r = i*ROWS_PER_LOAD + r0, 16-byte chunk c0
+  // (r0, c0 fixed per lane), into LDS slot i*256 + tid.  The buffer starts at the tile and
+  // holds the bytes left in K (V), so rows past Lk read as zeros (their scores are masked,
+  // their weights zero).  The K swizzle depends on i only through its parity (when a round
+  // covers 8 rows), the V swizzle not at all.
+  uint32_t vk[2], vv;
+  {
+    const int pos0 = wave * 64 + lane;
+    const int r0 = pos0 / CPR, c0 = pos0 % CPR;
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int pos = i * attn_cfg::kThreads + wave * 64 + lane;
-    const int r = pos / CPR, c = pos % CPR;
-    voff_k[i] = static_cast<uint32_t>(r * D * 2 + (c ^ swz_k(r)) * 16);
-    voff_v[i] = static_cast<uint32_t>(r * D * 2 + (c ^ swz_v(r)) * 16);
+    for (int par = 0; par < 2; ++par)
+      vk[par] = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_k(par * ROWS_PER_LOAD + r0)) * 16);
+    vv = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
   }
   const uint32_t kv_bytes = static_cast<uint32_t>(Lk) * D * 2;
   auto issue_tile = [&](int t, int st) {
     uint16_t* ks = smem + st * 2 * TILE;
     uint16_t* vs = ks + TILE;
-    const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // bytes before tile t
-    const i32x4 rk = make_rsrc(kh + (size_t)t * TILE, kv_bytes - skip);
-    const i32x4 rv = make_rsrc(vh + (size_t)t * TILE, kv_bytes - skip);
+    const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // t < ntiles: skip < kv_bytes
+    const i32x4 rk = make_rsrc(reinterpret_cast<const char*>(kh) + skip, kv_bytes - skip);
+    const i32x4 rv = make_rsrc(reinterpret_cast<const char*>(vh) + skip, kv_bytes - skip);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int slot0 = i * attn_cfg::kThreads + wave * 64;  // wave-uniform first slot
-      lds_dma16(rk, voff_k[i], ks + slot0 * 8);
-      lds_dma16(rv, voff_v[i], vs + slot0 * 8);
+      const uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
+      lds_dma16(rk, vk[i & 1] + rows, ks + slot0 * 8);
+      lds_dma16(rv, vv + rows, vs + slot0 * 8);
     }
   };
 
@@ -252,26 +261,28 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   if (ntiles > 1) issue_tile(1, 1);
   if (tid < 2) restart_flag[tid] = 0;  // 0 never matches an iteration number (read at it >= 1)
 
-  // Per-lane LDS element offsets of the fragment reads (stage base added later).
-  // K (A operand of S^T): row l%32, chunk 2kk+hi, permuted; kk = 4g+u splits into a
-  // lane-dependent part (u) and an immediate (64*g elements).
-  int koff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) koff[u] = l32 * D + (((2 * u + hi) ^ swz_k(l32)) * 8);
+  // ---- per-lane LDS byte offsets of the fragment reads (stage base added later) ----
+  // K (A operand of S^T): row l%32, chunk 2kk+hi at slot (2kk+hi) ^ sw, sw = swz_k(l%32);
+  // in bytes that is (32kk) ^ k0 with k0 below 256, added to the row start.
+  const int sw = swz_k(l32);
+  const uint32_t krow = static_cast<uint32_t>(l32 * D * 2);
+  const uint32_t k0 = static_cast<uint32_t>(16 * (hi ^ (sw & 1)) + 32 * (sw >> 1));
   // V^T (A operand of O^T) through ds_read_b64_tr_b16: in each 16-lane block, source lane
   // 4e+c supplies row (key) e, 4 dims at 4c of the block's 16 dims; lane i then receives
   // dim i of those 4 rows.  Lane block b16 = lane/16: half h = b16/2 selects keys 4h..4h+3
-  // (of each group of 8), b16%2 selects dims 16..31 of the 32-dim block.
-  int voff[2];
+  // (of each group of 8), b16%2 selects dims 16..31 of the 32-dim block db.  The chunk of
+  // those dims sits at slot (4db + 2*(b16%2) + c/2) ^ 4e: in bytes (64db) ^ v0, v0 < 256;
+  // db = 4g + u gives voffs[u] plus an immediate 256g.
+  uint32_t voffs[4];
   {
     const int b16 = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
     const int h = b16 >> 1, dh = b16 & 1;
+    const uint32_t v0 = static_cast<uint32_t>(16 * (2 * dh + (c >> 1)) + 64 * e);
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int chunk = 4 * par + 2 * dh + (c >> 1);
-      voff[par] = (4 * h + e) * D + ((chunk ^ swz_v(4 * h + e)) * 8) + (c & 1) * 4;
-    }
+    for (int u = 0; u < 4; ++u)
+      voffs[u] = static_cast<uint32_t>((4 * h + e) * D * 2 + (c & 1) * 8) + ((64u * u) ^ v0);
   }
+  const char* const smem_b = reinterpret_cast<const char*>(smem);
 
   // Output accumulator O^T, block (qb, db) = AGPR block qb*DB + db (attn_agpr.h).
   float m[QB], l[QB];
@@ -284,58 +295,50 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   }
   const float c = p.c;
 
-  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  // The key loop.  `it` counts iterations including restarts (see below) and never resets,
-  // so the restart flags written in one iteration cannot be mistaken for another's.
-  int t = 0;
-  for (int it = 0;; ++it) {
-    // Tile t was issued two iterations ago (or in the prologue); only tile t+1 may still be
-    // in flight, so wait for all but this thread's copies of tile t+1.
-    if (t + 1 < ntiles) WAIT_VMCNT(2 * LOADS);
-    else WAIT_VMCNT(0);
-    __syncthreads();  // everyone's share of tile t landed; stage of tile t-1 is free
-    // Restart.  A wave whose row maximum outgrew its reference m by more than kTau in the
-    // previous iteration raised m and flagged it; every wave then starts the key sweep over
-    // with zeroed accumulators (the waves' references stay valid).  This replaces the usual
-    // per-tile rescale of the output accumulator by alpha = exp2(m_old - m_new): the
-    // accumulator is only ever written by MFMAs, and with the first tile fixing m the
-    // restart is rare (the scores must grow by more than 2^kTau over the first tile's).
-    if (it > 0 && __builtin_amdgcn_readfirstlane(restart_flag[(it - 1) & 1]) == it) {
-      WAIT_VMCNT(0);
-      __syncthreads();  // nobody still reads a stage
-      issue_tile(0, 0);
-      if (ntiles > 1) issue_tile(1, 1);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        l[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) attn_agpr::zero(qb * DB + db);
-      }
-      t = 0;
-      continue;
-    }
-    if (t >= ntiles) break;
-    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
-    const uint16_t* ks = smem + (t % NSTAGE) * 2 * TILE;
-    const uint16_t* vs = ks + TILE;
-
-    // ---- S^T = K Q^T (fp32 accumulation) ----
-    f32x16 sacc[QB];
+  // ---- building blocks of one key-loop iteration ----
+  // S^T(t) = K(t) Q^T, fp32 accumulation, both query blocks sharing each K fragment.
+  // K fragments are prefetched two steps ahead; the scheduling barriers keep the compiler
+  // from hoisting all of them (64 registers) to the front.
+  auto qk = [&](const char* ks, f32x16 (&sacc)[QB]) {
+    auto kfrag = [&](int kk) {
+      return *reinterpret_cast<const u32x4*>(ks + krow + ((32u * kk) ^ k0));
+    };
+    u32x4 kf[3];
+    kf[0] = kfrag(0);
+    kf[1] = kfrag(1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(ks + koff[kk & 3] + (kk >> 2) * 64);
+      if (kk + 2 < KS) kf[(kk + 2) % 3] = kfrag(kk + 2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if (kk == 0) Elt<T>::mfma_v0(a, qf[qb][kk], sacc[qb]);
-        else Elt<T>::mfma_v(a, qf[qb][kk], sacc[qb]);
+        if (kk == 0) Elt<T>::mfma_v0(kf[kk % 3], qf[qb][kk], sacc[qb]);
+        else Elt<T>::mfma_v(kf[kk % 3], qf[qb][kk], sacc[qb]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mfma_fence_v(sacc[qb]);
-    // Keys past Lk (last tile only): the score becomes the worst value, so the key drops out
-    // of the maximum and its weight exp2(c*score - m) is exactly 0.  Accumulator register r
-    // of this lane holds key t*BN + 8*(r/4) + 4*hi + r%4.
+  };
+  // One P.V step of tile t-1: V^T fragment (32 dims x 16 keys) times both P^T blocks.
+  // MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator registers
+  // 8ks..8ks+7, whose keys for lane half h are 16ks + {4h..4h+3, 8+4h..8+4h+3}: the two
+  // transposing reads (rows +0 and +8) fetch exactly those rows of V.
+  auto pv_frag = [&](const char* vs, int s) -> u32x4 {
+    const int db = s >> 1, ks16 = s & 1;
+    const char* base = vs + voffs[db & 3] + 256 * (db >> 2) + 16 * ks16 * D * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * D * 2));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+    return (u32x4){lo2[0], lo2[1], up2[0], up2[1]};
+  };
+
+  // Online softmax of tile t, fp32 in base 2, split in two phases so that the P.V MFMAs of
+  // tile t-1 can run underneath.  Phase A: this tile's row maximum and the reference
+  // check.  Phase B: P = exp2(c*s - m) element by element, row sums, rounding to 16 bits.
+  float mt[QB];
+  auto phase_a = [&](f32x16 (&sacc)[QB], int t, int it) {
     if (t == nfull) {
+      // Keys past Lk (last tile only): the score becomes the worst value, so the key drops
+      // out of the maximum and its weight exp2(c*score - m) is exactly 0.  Accumulator
+      // register r of this lane holds key t*BN + 8*(r/4) + 4*hi + r%4.
       const int kvalid = Lk - t * BN - 4 * hi;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -343,18 +346,16 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) >= kvalid) sacc[qb][r] = kWorst;
     }
-
-    // ---- online softmax (fp32, base 2) ----
-    float mt[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float x = kWorst;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x = NEG ? fminf(x, sacc[qb][r]) : fmaxf(x, sacc[qb][r]);
-      }
-      const float y = __shfl_xor(x, 32);
-      x = NEG ? fminf(x, y) : fmaxf(x, y);
+      for (int r = 0; r < 16; ++r) x = NEG ? fminf(x, sacc[qb][r]) : fmaxf(x, sacc[qb][r]);
+      // the other 16 keys of this row sit in lane l^32
+      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+      const float y0 = __uint_as_float(sw2[0]), y1 = __uint_as_float(sw2[1]);
+      x = NEG ? fminf(y0, y1) : fmaxf(y0, y1);
       mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
     }
     if (t == 0) {
@@ -370,55 +371,112 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       }
       if (__builtin_amdgcn_ballot_w64(grow) != 0 && lane == 0) restart_flag[it & 1] = it + 1;
     }
-    u32x4 pb[QB][2];
+  };
+  // Phase B, elements [e0, e1) of 32: element e is register r = e%16 of query block e/16.
+  float ev[QB][16];
+  auto phase_b = [&](f32x16 (&sacc)[QB], u32x4 (&pcur)[QB][2], int e0, int e1) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      const int qb = e >> 4, r = e & 15;
+      ev[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -m[qb]));
+      l[qb] += ev[qb][r];
+      if (r & 1) pcur[qb][r >> 3][(r & 7) >> 1] = Elt<T>::pack2(ev[qb][r - 1], ev[qb][r]);
+    }
+  };
+
+  // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
+  // interleaved with the softmax of tile t.  PV: tile t-1 exists; SM: tile t exists.
+  u32x4 pprev[QB][2], pcur[QB][2];
+  auto iteration = [&](auto pv_tag, auto sm_tag, int t, int it) {
+    constexpr bool PV = decltype(pv_tag)::value;
+    constexpr bool SM = decltype(sm_tag)::value;
+    const char* const vs_prev = smem_b + ((t + NSTAGE - 1) % NSTAGE) * 4 * TILE + TILE * 2;
+    f32x16 sacc[QB];
+    if constexpr (SM) qk(smem_b + (t % NSTAGE) * 4 * TILE, sacc);
+    u32x4 vfrag[2];
+    if constexpr (PV) vfrag[0] = pv_frag(vs_prev, 0);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if constexpr (PV) {
+        if (s + 1 < NSTEP) vfrag[(s + 1) & 1] = pv_frag(vs_prev, s + 1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          Elt<T>::acc_mfma(qb * DB + (s >> 1), vfrag[s & 1], pprev[qb][s & 1]);
+      }
+      if constexpr (SM) {
+        if (s == 0) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) mfma_fence_v(sacc[qb]);
+          phase_a(sacc, t, it);
+        } else {
+          // the 32 exponentials spread over steps 1..NSTEP-1
+          phase_b(sacc, pcur, 32 * (s - 1) / (NSTEP - 1), 32 * s / (NSTEP - 1));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SM) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) pprev[qb][k2] = pcur[qb][k2];
+    }
+  };
+
+  // ---- the key loop ----
+  // `it` counts barrier-separated iterations including restarts and never resets, so the
+  // restart flags written in one iteration cannot be mistaken for another's.  Restart: a
+  // wave whose row maximum outgrew its reference m by more than kTau raised m and flagged
+  // it; at the next iteration every wave starts the key sweep over with zeroed accumulators
+  // (the references stay valid).  This replaces the usual per-tile rescale of the output
+  // accumulator by exp2(m_old - m_new): the accumulator is only ever written by MFMAs, and
+  // with the first tile fixing m a restart needs the scores to grow by more than 2^kTau.
+  int it = 0;
+  for (;;) {
+    bool restart = false;
+    for (int t = 0; t <= ntiles; ++t, ++it) {
+      // Tile t was issued two iterations ago (or in the prologue); only tile t+1 may still
+      // be in flight, so wait for all but this thread's copies of tile t+1.
+      if (t + 1 < ntiles) WAIT_VMCNT(2 * LOADS);
+      else WAIT_VMCNT(0);
+      __syncthreads();  // tile t landed everywhere; stage of tile t-2 is free
+      if (it > 0 && __builtin_amdgcn_readfirstlane(restart_flag[(it - 1) & 1]) == it) {
+        restart = true;
+        ++it;
+        break;
+      }
+      if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
+      if (t == 0) iteration(std::false_type{}, std::true_type{}, t, it);
+      else if (t < ntiles) iteration(std::true_type{}, std::true_type{}, t, it);
+      else iteration(std::true_type{}, std::false_type{}, t, it);  // drain: P.V of the last tile
+    }
+    if (!restart) {
+      // a growth flagged in the last softmax iteration is seen by the drain iteration's
+      // check; nothing can be flagged after it
+      break;
+    }
+    WAIT_VMCNT(0);
+    __syncthreads();  // nobody still reads a stage
+    issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float mneg = -m[qb];
-      float pv[16];
-      float sum = 0.f;
+      l[qb] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, mneg));
-        pv[r] = e;
-        sum += e;
-      }
-      l[qb] += sum;
-#pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8)
-        pb[qb][h8] = (u32x4){Elt<T>::pack2(pv[8 * h8 + 0], pv[8 * h8 + 1]),
-                             Elt<T>::pack2(pv[8 * h8 + 2], pv[8 * h8 + 3]),
-                             Elt<T>::pack2(pv[8 * h8 + 4], pv[8 * h8 + 5]),
-                             Elt<T>::pack2(pv[8 * h8 + 6], pv[8 * h8 + 7])};
+      for (int db = 0; db < DB; ++db) attn_agpr::zero(qb * DB + db);
     }
-
-    // ---- O^T += V^T P^T ----
-    // MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator registers
-    // 8ks..8ks+7, whose keys for lane half h are 16ks + {4h..4h+3, 8+4h..8+4h+3}: the two
-    // transposing reads (rows +0 and +8) fetch exactly those rows of V.
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int ks16 = 0; ks16 < 2; ++ks16) {
-        const uint16_t* base = vs + voff[db & 1] + (db >> 1) * 64 + 16 * ks16 * D;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-        const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * D));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
-        const u32x4 a = {lo2[0], lo2[1], up2[0], up2[1]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) Elt<T>::acc_mfma(qb * DB + db, a, pb[qb][ks16]);
-      }
-    }
-    ++t;
   }
 
   // Epilogue: O = O^T / l (one reciprocal per row), LSE = ln2 * (m + log2 l).
   attn_agpr::fence();
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));  // recompute row addresses here instead of keeping them
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l[qb] + __shfl_xor(l[qb], 32);
     const float inv = 1.0f / lt;
-    const int row = qrow0 + qb * 32 + l32;
-    uint16_t* dst = p.o + ((size_t)bh * p.Lq + min(row, p.Lq - 1)) * D + 4 * hi;
+    const int row = qrow0 + qb * 32 + (lane_e & 31);
+    uint16_t* dst = p.o + ((size_t)bh * p.Lq + min(row, p.Lq - 1)) * D + 4 * (lane_e >> 5);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       float x[16];

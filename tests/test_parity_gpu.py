@@ -194,3 +194,38 @@ def test_scale_sign_and_zero():
     mean = v.double().mean(dim=2, keepdim=True)
     assert (o.double() - mean).abs().max().item() <= 2e-3
     assert (lse.double() - math.log(160)).abs().max().item() <= 1e-5
+
+
+def _growing_scores(D, dt, Lk, spikes, seed):
+    """Inputs whose per-row maximum score jumps far above the first key tile's maximum at
+    the given key positions, so the kernel's softmax reference must be raised mid-sweep.
+    Every query gets a shared component 2*u (u a random unit vector); key `pos` is mult*u,
+    so its score is about scale*mult*(2 +- 1) for every row."""
+    q, k, v = attn_inputs.make_qkv(1, 4, 2, 200, Lk, D, dt, seed=seed)
+    g = torch.Generator().manual_seed(seed + 99)
+    u = torch.randn(D, generator=g, dtype=torch.float64)
+    u = u / u.norm()
+    q = (q.double() + 2.0 * u).to(q.dtype)
+    for pos, mult in spikes:
+        k[0, :, pos] = (u * mult).to(k.dtype)
+    return q, k, v
+
+
+@pytest.mark.parametrize("D,dt", [(256, "f16"), (128, "bf16"), (256, "bf16")])
+def test_reference_growth_mid_sweep(D, dt):
+    """A score far above the first tile's maximum in a later tile (forces the kernel to
+    restart its key sweep with a higher reference)."""
+    _announce("growth mid sweep D=%d %s" % (D, dt))
+    q, k, v = _growing_scores(D, dt, 700, [(333, 300.0)], seed=21)
+    parity(q, k, v, scale_of(D), dt, what="growth mid")
+
+
+def test_reference_growth_last_tile_and_repeated():
+    """Growth in the very last (ragged) key tile, and several successive jumps."""
+    _announce("growth last tile / repeated")
+    D = 256
+    q, k, v = _growing_scores(D, "f16", 641, [(640, 400.0)], seed=22)
+    parity(q, k, v, scale_of(D), "f16", what="growth last key")
+    q, k, v = _growing_scores(D, "f16", 900, [(100, 150.0), (300, 300.0), (500, 450.0),
+                                              (899, 600.0)], seed=23)
+    parity(q, k, v, scale_of(D), "f16", what="growth repeated")
