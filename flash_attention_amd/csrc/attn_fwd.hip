@@ -62,18 +62,20 @@ struct Params {
 // 32x32x16 MFMA issued through inline asm.  The score accumulator is pinned to VGPRs ("v":
 // the softmax reads it with VALU instructions); the output accumulator lives in fixed AGPRs
 // (attn_agpr.h), written only by MFMAs inside the key loop.  The compiler does not look for
-// hazards inside inline asm, so the statements carry their own wait states: 3 before each
-// MFMA (a source may have been written by the VALU instruction just before; the ISA asks
-// for 2), and every reader of an MFMA result is ordered behind a fence of 24 wait states
-// (an 8-pass XDL result needs NumPasses + 3 before a VALU read).
+// hazards inside inline asm.  The MFMA sources here are LDS/global loads or VALU results
+// written far earlier, so no wait states precede the MFMAs (each s_nop in front of one
+// costs about a tenth of the matrix-core rate); tests/test_kernel_asm.py checks on the
+// emitted code that no VALU write lands within 2 wait states of an MFMA reading it.  Every
+// VALU reader of an MFMA result is ordered behind a fence of 24 wait states (an 8-pass XDL
+// result needs NumPasses + 3), also checked there.
 #define ATTN_MFMA_F16 "v_mfma_f32_32x32x16_f16"
 #define ATTN_MFMA_BF16 "v_mfma_f32_32x32x16_bf16"
 #define ATTN_MFMA_STMTS(OPC)                                                              \
   static __device__ __forceinline__ void mfma_v0(u32x4 a, u32x4 b, f32x16& c) {           \
-    asm volatile("s_nop 2\n\t" OPC " %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));          \
+    asm volatile(OPC " %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));                        \
   }                                                                                       \
   static __device__ __forceinline__ void mfma_v(u32x4 a, u32x4 b, f32x16& c) {            \
-    asm volatile("s_nop 2\n\t" OPC " %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));          \
+    asm volatile(OPC " %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));                        \
   }
 
 template <typename T>

@@ -73,3 +73,141 @@ def test_no_scratch(asm):
 def test_no_packed_fp32(asm):
     for name, lines in kernels(asm).items():
         assert not [ln for ln, _ in lines if re.match(r"v_pk_(fma|mul|add)_f32", ln)], name
+
+
+# ---- MFMA hazard check ------------------------------------------------------------------
+# The MFMAs are inline asm, so the compiler inserts no wait states around them.  The ISA
+# requires (gfx940 family): 2 wait states between a VALU write of a VGPR and an MFMA reading
+# it, and NumPasses + 3 between an MFMA writing a register and a VALU access to it (11 for
+# the 8-pass 32x32x16 ops; 18 is checked here).  MFMA -> MFMA accumulation into the same
+# registers is interlocked by the hardware.  These checks walk the emitted code.
+REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)\b)")
+
+
+def regs_of(text):
+    out = set()
+    for m in REG.finditer(text):
+        kind = m.group(1)
+        if m.group(4) is not None:
+            out.add((kind, int(m.group(4))))
+        else:
+            out.update((kind, i) for i in range(int(m.group(2)), int(m.group(3)) + 1))
+    return out
+
+
+def split_ops(ln):
+    parts = ln.split(None, 1)
+    op = parts[0]
+    args = [a.strip() for a in parts[1].split(",")] if len(parts) > 1 else []
+    return op, args
+
+
+def wait_states(ln):
+    op, args = split_ops(ln)
+    if op == "s_nop":
+        return int(args[0], 0) + 1
+    return 1
+
+
+def is_valu(op):
+    return op.startswith("v_") and not op.startswith("v_mfma") and op not in (
+        "v_readfirstlane_b32", "v_readlane_b32")
+
+
+def valu_defs(ln):
+    op, args = split_ops(ln)
+    if not args:
+        return set()
+    d = regs_of(args[0])
+    if op in ("v_permlane32_swap_b32", "v_permlane16_swap_b32", "v_swap_b32") and len(args) > 1:
+        d |= regs_of(args[1])
+    return d
+
+
+def instruction_stream(text):
+    """Per kernel: list of (line, in_asm, is_label)."""
+    res = {}
+    for m in re.finditer(r"^(_Z\w*attn_fwd_kernel\w*):[^\n]*\n(.*?)^\s*s_endpgm", text,
+                         re.M | re.S):
+        seq, inside = [], False
+        for ln in m.group(2).splitlines():
+            s = ln.strip()
+            if s.startswith(";;#ASMSTART"):
+                inside = True
+            elif s.startswith(";;#ASMEND"):
+                inside = False
+            elif re.match(r"^\.?[A-Za-z_][\w.]*:", s):
+                seq.append((s, inside, True))
+            elif s and not s.startswith(";") and not s.startswith("."):
+                seq.append((s.split(";")[0].strip(), inside, False))
+        res[m.group(1)] = seq
+    return res
+
+
+def test_mfma_source_hazards(asm):
+    """No VALU instruction writes an MFMA source register less than 2 wait states before."""
+    problems = []
+    for name, seq in instruction_stream(asm).items():
+        for i, (ln, _, lab) in enumerate(seq):
+            if lab or not ln.startswith("v_mfma"):
+                continue
+            op, args = split_ops(ln)
+            srcs = set()
+            for a in args[1:]:
+                srcs |= regs_of(a)
+            ws, j = 0, i - 1
+            while j >= 0 and ws < 2:
+                pln, _, plab = seq[j]
+                if plab:
+                    problems.append((name, "label before MFMA within 2 wait states", ln))
+                    break
+                pop, _ = split_ops(pln)
+                if is_valu(pop) and valu_defs(pln) & srcs:
+                    problems.append((name, pln, ln))
+                    break
+                ws += wait_states(pln)
+                j -= 1
+    assert not problems, problems[:6]
+
+
+def test_mfma_result_hazards(asm):
+    """No VALU instruction touches an MFMA destination less than 18 wait states after it."""
+    problems = []
+    for name, seq in instruction_stream(asm).items():
+        for i, (ln, _, lab) in enumerate(seq):
+            if lab or not ln.startswith("v_mfma"):
+                continue
+            op, args = split_ops(ln)
+            dst = regs_of(args[0])
+            ws, j = 0, i + 1
+            while j < len(seq) and ws < 18:
+                nln, _, nlab = seq[j]
+                if nlab or nln.startswith("s_cbranch") or nln.startswith("s_branch"):
+                    break
+                nop, nargs = split_ops(nln)
+                if is_valu(nop):
+                    touched = set()
+                    for a in nargs:
+                        touched |= regs_of(a)
+                    if touched & dst:
+                        problems.append((name, ln, nln, ws))
+                        break
+                ws += wait_states(nln)
+                j += 1
+    assert not problems, problems[:6]
+
+
+def test_hazard_checker_catches_planted_hazards():
+    """The two checkers flag a VALU write right before an MFMA source and a VALU read right
+    after an MFMA result (planted in a synthetic stream, not in the kernels)."""
+    good = ("_Zattn_fwd_kernel_t:\n\tds_read_b128 v[4:7], v1\n\ts_waitcnt lgkmcnt(0)\n"
+            "\ts_nop 1\n\tv_mfma_f32_32x32x16_f16 a[0:15], v[4:7], v[8:11], a[0:15]\n"
+            "\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_accvgpr_read_b32 v2, a3\n\ts_endpgm\n")
+    bad_src = good.replace("\ts_nop 1\n", "\tv_mov_b32_e32 v9, 0\n")
+    bad_dst = good.replace("\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n", "\ts_nop 3\n")
+    test_mfma_source_hazards(good)
+    test_mfma_result_hazards(good)
+    with pytest.raises(AssertionError):
+        test_mfma_source_hazards(bad_src)
+    with pytest.raises(AssertionError):
+        test_mfma_result_hazards(bad_dst)
