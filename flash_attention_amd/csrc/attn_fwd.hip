@@ -203,10 +203,12 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const int xcd = bid & 7, local = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
-  const int qtile = logical % p.n_qtiles;
-  const int bh = logical / p.n_qtiles;  // b*Hq + hq
-  const int hq = bh % p.Hq, b = bh / p.Hq;
-  const int hkv = hq / p.G;
+  // (integer division is expanded into VALU code; readfirstlane keeps the results in SGPRs)
+  const int qtile = __builtin_amdgcn_readfirstlane(logical % p.n_qtiles);
+  const int bh = __builtin_amdgcn_readfirstlane(logical / p.n_qtiles);  // b*Hq + hq
+  const int hq = __builtin_amdgcn_readfirstlane(bh % p.Hq);
+  const int b = __builtin_amdgcn_readfirstlane(bh / p.Hq);
+  const int hkv = __builtin_amdgcn_readfirstlane(hq / p.G);
 
   const uint16_t* qh = p.q + (size_t)bh * p.Lq * D;
   const uint16_t* kh = p.k + ((size_t)b * p.Hkv + hkv) * p.Lk * D;
@@ -298,19 +300,19 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const float c = p.c;
 
   // ---- building blocks of one key-loop iteration ----
-  // S^T(t) = K(t) Q^T, fp32 accumulation, both query blocks sharing each K fragment.
-  // K fragments are prefetched two steps ahead; the scheduling barriers keep the compiler
-  // from hoisting all of them (64 registers) to the front.
-  auto qk = [&](const char* ks, f32x16 (&sacc)[QB]) {
-    auto kfrag = [&](int kk) {
-      return *reinterpret_cast<const u32x4*>(ks + krow + ((32u * kk) ^ k0));
-    };
-    u32x4 kf[3];
-    kf[0] = kfrag(0);
-    kf[1] = kfrag(1);
+  auto kstage = [&](int t) { return smem_b + (t % NSTAGE) * 4 * TILE; };
+  auto vstage = [&](int t) { return smem_b + (t % NSTAGE) * 4 * TILE + TILE * 2; };
+  // K fragment kk of a tile: the A operand of S^T step kk.
+  auto kfrag = [&](const char* ks, int kk) {
+    return *reinterpret_cast<const u32x4*>(ks + krow + ((32u * kk) ^ k0));
+  };
+  // S^T(t) = K(t) Q^T, fp32 accumulation, both query blocks sharing each K fragment.  The
+  // first two fragments arrive prefetched in kf[0..1]; the rest are fetched two steps ahead,
+  // and the scheduling barriers keep the compiler from hoisting all of them (64 registers).
+  auto qk = [&](const char* ks, f32x16 (&sacc)[QB], u32x4 (&kf)[3]) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      if (kk + 2 < KS) kf[(kk + 2) % 3] = kfrag(kk + 2);
+      if (kk + 2 < KS) kf[(kk + 2) % 3] = kfrag(ks, kk + 2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (kk == 0) Elt<T>::mfma_v0(kf[kk % 3], qf[qb][kk], sacc[qb]);
@@ -319,11 +321,11 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // One P.V step of tile t-1: V^T fragment (32 dims x 16 keys) times both P^T blocks.
-  // MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator registers
-  // 8ks..8ks+7, whose keys for lane half h are 16ks + {4h..4h+3, 8+4h..8+4h+3}: the two
-  // transposing reads (rows +0 and +8) fetch exactly those rows of V.
-  auto pv_frag = [&](const char* vs, int s) -> u32x4 {
+  // One P.V step s of a tile: V^T fragment (32 dims x 16 keys) for MFMA step s, times both
+  // P^T blocks.  MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator
+  // registers 8ks..8ks+7, whose keys for lane half h are 16ks + {4h..4h+3, 8+4h..8+4h+3}:
+  // the two transposing reads (rows +0 and +8) fetch exactly those rows of V.
+  auto vfrag_load = [&](const char* vs, int s) -> u32x4 {
     const int db = s >> 1, ks16 = s & 1;
     const char* base = vs + voffs[db & 3] + 256 * (db >> 2) + 16 * ks16 * D * 2;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
@@ -332,15 +334,15 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     return (u32x4){lo2[0], lo2[1], up2[0], up2[1]};
   };
 
-  // Online softmax of tile t, fp32 in base 2, split in two phases so that the P.V MFMAs of
-  // tile t-1 can run underneath.  Phase A: this tile's row maximum and the reference
-  // check.  Phase B: P = exp2(c*s - m) element by element, row sums, rounding to 16 bits.
+  // Online softmax of tile t, fp32 in base 2, in slices that run underneath the P.V MFMAs
+  // of tile t-1.  Max slices: this tile's row maximum per query block, then the reference
+  // check.  Exp slices: P = exp2(c*s - m) element by element, row sums, rounding to 16 bits.
   float mt[QB];
-  auto phase_a = [&](f32x16 (&sacc)[QB], int t, int it) {
+  auto mask_tail = [&](f32x16 (&sacc)[QB], int t) {
+    // Keys past Lk (last tile only): the score becomes the worst value, so the key drops
+    // out of the maximum and its weight exp2(c*score - m) is exactly 0.  Accumulator
+    // register r of this lane holds key t*BN + 8*(r/4) + 4*hi + r%4.
     if (t == nfull) {
-      // Keys past Lk (last tile only): the score becomes the worst value, so the key drops
-      // out of the maximum and its weight exp2(c*score - m) is exactly 0.  Accumulator
-      // register r of this lane holds key t*BN + 8*(r/4) + 4*hi + r%4.
       const int kvalid = Lk - t * BN - 4 * hi;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -348,18 +350,19 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) >= kvalid) sacc[qb][r] = kWorst;
     }
+  };
+  auto row_max = [&](f32x16 (&sacc)[QB], int qb) {
+    float x = kWorst;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float x = kWorst;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x = NEG ? fminf(x, sacc[qb][r]) : fmaxf(x, sacc[qb][r]);
-      // the other 16 keys of this row sit in lane l^32
-      const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                        false, false);
-      const float y0 = __uint_as_float(sw2[0]), y1 = __uint_as_float(sw2[1]);
-      x = NEG ? fminf(y0, y1) : fmaxf(y0, y1);
-      mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
-    }
+    for (int r = 0; r < 16; ++r) x = NEG ? fminf(x, sacc[qb][r]) : fmaxf(x, sacc[qb][r]);
+    // the other 16 keys of this row sit in lane l^32
+    const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                      false, false);
+    const float y0 = __uint_as_float(sw2[0]), y1 = __uint_as_float(sw2[1]);
+    x = NEG ? fminf(y0, y1) : fmaxf(y0, y1);
+    mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
+  };
+  auto check_reference = [&](int t, int it) {
     if (t == 0) {
       // Nothing accumulated yet: the first tile just sets the reference.
 #pragma unroll
@@ -374,11 +377,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       if (__builtin_amdgcn_ballot_w64(grow) != 0 && lane == 0) restart_flag[it & 1] = it + 1;
     }
   };
-  // Phase B, elements [e0, e1) of 32: element e is register r = e%16 of query block e/16.
   float ev[QB][16];
-  auto phase_b = [&](f32x16 (&sacc)[QB], u32x4 (&pcur)[QB][2], int e0, int e1) {
+  auto exp_slice = [&](f32x16 (&sacc)[QB], u32x4 (&pcur)[QB][2], int e0, int e1) {
 #pragma unroll
-    for (int e = e0; e < e1; ++e) {
+    for (int e = e0; e < e1; ++e) {  // element e: register e%16 of query block e/16
       const int qb = e >> 4, r = e & 15;
       ev[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -m[qb]));
       l[qb] += ev[qb][r];
@@ -386,75 +388,109 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     }
   };
 
+  // Synchronisation point of iteration t (in the middle of its P.V steps): tile t+1 has
+  // landed everywhere, every wave is past iteration t-1 so the stage of tile t-2 can take
+  // tile t+2, and the restart flags written before it are visible.
+  auto sync_point = [&](int t, int it) -> int {
+    if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of tile t+1
+    __syncthreads();
+    const int flag = restart_flag[it & 1];  // consumed at the end of the iteration
+    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
+    return flag;
+  };
+
   // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
-  // interleaved with the softmax of tile t.  PV: tile t-1 exists; SM: tile t exists.
-  u32x4 pprev[QB][2], pcur[QB][2];
-  auto iteration = [&](auto pv_tag, auto sm_tag, int t, int it) {
+  // (PV) with the softmax of tile t in slices underneath.  Returns true for a restart.
+  constexpr int SYNC_STEP = NSTEP - 3;  // two P.V steps remain after the sync point
+  u32x4 kf[3];
+  auto iteration = [&](auto pv_tag, int t, int it, u32x4 (&pprev)[QB][2],
+                       u32x4 (&pcur)[QB][2]) -> bool {
     constexpr bool PV = decltype(pv_tag)::value;
-    constexpr bool SM = decltype(sm_tag)::value;
-    const char* const vs_prev = smem_b + ((t + NSTAGE - 1) % NSTAGE) * 4 * TILE + TILE * 2;
     f32x16 sacc[QB];
-    if constexpr (SM) qk(smem_b + (t % NSTAGE) * 4 * TILE, sacc);
-    u32x4 vfrag[2];
-    if constexpr (PV) vfrag[0] = pv_frag(vs_prev, 0);
+    qk(kstage(t), sacc, kf);
+    const char* const vs = vstage(t + NSTAGE - 1);  // tile t-1
+    u32x4 vf[3];
+    if constexpr (PV) {
+      vf[0] = vfrag_load(vs, 0);
+      vf[1] = vfrag_load(vs, 1);
+    }
+    int flag = 0;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if constexpr (PV) {
-        if (s + 1 < NSTEP) vfrag[(s + 1) & 1] = pv_frag(vs_prev, s + 1);
+        if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(vs, s + 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          Elt<T>::acc_mfma(qb * DB + (s >> 1), vfrag[s & 1], pprev[qb][s & 1]);
+          Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pprev[qb][s & 1]);
       }
-      if constexpr (SM) {
-        if (s == 0) {
+      if (s == 0) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) mfma_fence_v(sacc[qb]);
-          phase_a(sacc, t, it);
-        } else {
-          // the 32 exponentials spread over steps 1..NSTEP-1
-          phase_b(sacc, pcur, 32 * (s - 1) / (NSTEP - 1), 32 * s / (NSTEP - 1));
-        }
+        for (int qb = 0; qb < QB; ++qb) mfma_fence_v(sacc[qb]);
+        mask_tail(sacc, t);
+        row_max(sacc, 0);
+      } else if (s == 1) {
+        row_max(sacc, 1);
+      } else if (s == 2) {
+        check_reference(t, it);
+      } else {
+        // the 32 exponentials spread over steps 3..NSTEP-1
+        exp_slice(sacc, pcur, 32 * (s - 3) / (NSTEP - 3), 32 * (s - 2) / (NSTEP - 3));
+      }
+      if (s == SYNC_STEP) flag = sync_point(t, it);
+      if (s == NSTEP - 1 && t + 1 < ntiles) {
+        // first two K fragments of tile t+1 (landed at the sync point)
+        kf[0] = kfrag(kstage(t + 1), 0);
+        kf[1] = kfrag(kstage(t + 1), 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (SM) {
+    return __builtin_amdgcn_readfirstlane(flag) == it + 1;
+  };
+  // P.V of the last tile (no softmax, no synchronisation).
+  auto drain = [&](int t, u32x4 (&pprev)[QB][2]) {
+    const char* const vs = vstage(t);
+    u32x4 vf[3];
+    vf[0] = vfrag_load(vs, 0);
+    vf[1] = vfrag_load(vs, 1);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(vs, s + 2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) pprev[qb][k2] = pcur[qb][k2];
+        Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pprev[qb][s & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---- the key loop ----
-  // `it` counts barrier-separated iterations including restarts and never resets, so the
-  // restart flags written in one iteration cannot be mistaken for another's.  Restart: a
-  // wave whose row maximum outgrew its reference m by more than kTau raised m and flagged
-  // it; at the next iteration every wave starts the key sweep over with zeroed accumulators
-  // (the references stay valid).  This replaces the usual per-tile rescale of the output
-  // accumulator by exp2(m_old - m_new): the accumulator is only ever written by MFMAs, and
-  // with the first tile fixing m a restart needs the scores to grow by more than 2^kTau.
+  // `it` counts iterations including restarts and never resets, so a restart flag written
+  // in one iteration cannot be mistaken for another's.  Restart: a wave whose row maximum
+  // outgrew its reference m by more than kTau raised m and flagged it before the sync
+  // point; at the end of that iteration every wave starts the key sweep over with zeroed
+  // accumulators (the references stay valid).  This replaces the usual per-tile rescale of
+  // the output accumulator by exp2(m_old - m_new): the accumulator is only ever written by
+  // MFMAs, and with the first tile fixing m a restart needs the scores to grow by more than
+  // 2^kTau.  The loop is unrolled by two so the P buffers swap roles without copies.
+  u32x4 pa[QB][2], pb2[QB][2];
   int it = 0;
   for (;;) {
-    bool restart = false;
-    for (int t = 0; t <= ntiles; ++t, ++it) {
-      // Tile t was issued two iterations ago (or in the prologue); only tile t+1 may still
-      // be in flight, so wait for all but this thread's copies of tile t+1.
-      if (t + 1 < ntiles) WAIT_VMCNT(2 * LOADS);
-      else WAIT_VMCNT(0);
-      __syncthreads();  // tile t landed everywhere; stage of tile t-2 is free
-      if (it > 0 && __builtin_amdgcn_readfirstlane(restart_flag[(it - 1) & 1]) == it) {
-        restart = true;
-        ++it;
-        break;
-      }
-      if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
-      if (t == 0) iteration(std::false_type{}, std::true_type{}, t, it);
-      else if (t < ntiles) iteration(std::true_type{}, std::true_type{}, t, it);
-      else iteration(std::true_type{}, std::false_type{}, t, it);  // drain: P.V of the last tile
+    if (ntiles > 1) WAIT_VMCNT(2 * LOADS);  // tile 0 landed (tile 1 may be in flight)
+    else WAIT_VMCNT(0);
+    __syncthreads();
+    kf[0] = kfrag(kstage(0), 0);
+    kf[1] = kfrag(kstage(0), 1);
+    bool restart = iteration(std::false_type{}, 0, it++, pb2, pa);
+    int t = 1;
+    while (!restart && t < ntiles) {
+      restart = iteration(std::true_type{}, t, it++, pa, pb2);  // P(t-1) in pa
+      ++t;
+      if (restart || t >= ntiles) break;
+      restart = iteration(std::true_type{}, t, it++, pb2, pa);  // P(t-1) in pb2
+      ++t;
     }
     if (!restart) {
-      // a growth flagged in the last softmax iteration is seen by the drain iteration's
-      // check; nothing can be flagged after it
+      if (ntiles & 1) drain(ntiles - 1, pa);  // P(t) lives in pa for even t
+      else drain(ntiles - 1, pb2);
       break;
     }
     WAIT_VMCNT(0);

@@ -144,10 +144,48 @@ def instruction_stream(text):
     return res
 
 
+def _branch_sources(seq):
+    """label -> indices of the branch instructions that jump to it."""
+    src = {}
+    for i, (ln, _, lab) in enumerate(seq):
+        if not lab and (ln.startswith("s_cbranch") or ln.startswith("s_branch")):
+            src.setdefault(ln.split()[-1], []).append(i)
+    return src
+
+
+def _preceding_writes(seq, branches, j, budget, srcs, seen):
+    """Walk back from instruction j over every control-flow predecessor until `budget` wait
+    states are covered; return the VALU lines that write one of `srcs` on the way."""
+    hits = []
+    while j >= 0 and budget > 0:
+        if (j, budget) in seen:
+            return hits
+        seen.add((j, budget))
+        ln, _, lab = seq[j]
+        if lab:
+            for b in branches.get(ln.rstrip(":").split()[0].rstrip(":"), []):
+                hits += _preceding_writes(seq, branches, b - 1, budget, srcs, seen)
+            prev = seq[j - 1][0] if j > 0 else ""
+            if prev.startswith("s_branch"):
+                return hits  # no fall-through into this label
+            j -= 1
+            continue
+        op, _ = split_ops(ln)
+        if is_valu(op) and valu_defs(ln) & srcs:
+            hits.append(ln)
+            return hits
+        if not op.startswith("s_cbranch") and not op.startswith("s_branch"):
+            budget -= wait_states(ln)
+        j -= 1
+    return hits
+
+
 def test_mfma_source_hazards(asm):
-    """No VALU instruction writes an MFMA source register less than 2 wait states before."""
+    """No VALU instruction writes an MFMA source register less than 2 wait states before, on
+    any control-flow path into the MFMA."""
     problems = []
     for name, seq in instruction_stream(asm).items():
+        branches = _branch_sources(seq)
         for i, (ln, _, lab) in enumerate(seq):
             if lab or not ln.startswith("v_mfma"):
                 continue
@@ -155,18 +193,9 @@ def test_mfma_source_hazards(asm):
             srcs = set()
             for a in args[1:]:
                 srcs |= regs_of(a)
-            ws, j = 0, i - 1
-            while j >= 0 and ws < 2:
-                pln, _, plab = seq[j]
-                if plab:
-                    problems.append((name, "label before MFMA within 2 wait states", ln))
-                    break
-                pop, _ = split_ops(pln)
-                if is_valu(pop) and valu_defs(pln) & srcs:
-                    problems.append((name, pln, ln))
-                    break
-                ws += wait_states(pln)
-                j -= 1
+            hits = _preceding_writes(seq, branches, i - 1, 2, srcs, set())
+            if hits:
+                problems.append((name, hits[0], ln))
     assert not problems, problems[:6]
 
 
