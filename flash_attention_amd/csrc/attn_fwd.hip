@@ -24,10 +24,12 @@
 // with one query per lane column as well.
 //
 // Pipeline.  K and V tiles of 32 keys are copied straight from HBM into LDS (no register
-// staging), three tiles resident: tile t+2 is in flight while tile t is consumed, with one
-// workgroup barrier per tile.  Each wavefront owns 64 query rows (two 32-row MFMA blocks),
-// so every K and V fragment read from LDS feeds two MFMAs; Q stays in registers and the
-// output accumulator in AGPRs for the whole key loop.
+// staging) into four stages.  Iteration t of the key loop reads K of tile t (S^T) and V of
+// tile t-1 (the P.V product of the previous tile, under which the softmax of tile t runs);
+// tile t+1 is landing, and tile t+2 is issued at the one workgroup barrier of the
+// iteration.  Each wavefront owns 64 query rows (two 32-row MFMA blocks), so every K and V
+// fragment read from LDS feeds two MFMAs; Q stays in registers and the output accumulator
+// in AGPRs for the whole key loop.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -112,6 +114,13 @@ __device__ __forceinline__ void mfma_fence_v(f32x16& x) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
+// Materialise x here: the compiler may not sink its computation past this point (the
+// softmax slices have to stay between the MFMAs they are meant to run under).
+template <typename X>
+__device__ __forceinline__ void pin(X& x) {
+  asm volatile("" : "+v"(x));
+}
+
 // ---------------------------------------------------------------------------------------
 // LDS layouts.  K and V tiles are stored row-major [key][d] exactly as in HBM, except that
 // the 16-byte chunks of each row are XOR-permuted so the fragment reads are bank-conflict
@@ -154,12 +163,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
                  __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
 }
 
-__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, const uint16_t* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)dst)));
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t lds_dst) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "s"(lds_dst), "v"(voffset), "s"(rsrc)
                : "memory");
 }
 
@@ -188,8 +195,12 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 
   extern __shared__ u32x4 smem_raw[];
   uint16_t* const smem = reinterpret_cast<uint16_t*>(smem_raw);
-  // Two restart flags after the K/V stages (written by at most one lane per wave).
-  volatile int* const restart_flag = reinterpret_cast<volatile int*>(smem + NSTAGE * 2 * TILE);
+  // Two restart flags after the K/V stages (written by at most one lane per wave), read
+  // through an LDS pointer so the read waits on LDS traffic only.
+  typedef __attribute__((address_space(3))) volatile int lds_vint;
+  lds_vint* const restart_flag = (lds_vint*)(smem + NSTAGE * 2 * TILE);
+  // LDS byte address of the stages, for the copy destinations (M0).
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)smem));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -234,18 +245,23 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     vv = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
   }
   const uint32_t kv_bytes = static_cast<uint32_t>(Lk) * D * 2;
+  const char* const kb = reinterpret_cast<const char*>(kh);
+  const char* const vb = reinterpret_cast<const char*>(vh);
   auto issue_tile = [&](int t, int st) {
-    uint16_t* ks = smem + st * 2 * TILE;
-    uint16_t* vs = ks + TILE;
+    const uint32_t ks = lds_base + static_cast<uint32_t>(st * 4 * TILE);
+    const uint32_t vs = ks + 2 * TILE;
     const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // t < ntiles: skip < kv_bytes
-    const i32x4 rk = make_rsrc(reinterpret_cast<const char*>(kh) + skip, kv_bytes - skip);
-    const i32x4 rv = make_rsrc(reinterpret_cast<const char*>(vh) + skip, kv_bytes - skip);
+    const i32x4 rk = make_rsrc(kb + skip, kv_bytes - skip);
+    const i32x4 rv = make_rsrc(vb + skip, kv_bytes - skip);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int slot0 = i * attn_cfg::kThreads + wave * 64;  // wave-uniform first slot
-      const uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
-      lds_dma16(rk, vk[i & 1] + rows, ks + slot0 * 8);
-      lds_dma16(rv, vv + rows, vs + slot0 * 8);
+      const uint32_t slot0 = (i * attn_cfg::kThreads + wave * 64) * 16;  // wave-uniform
+      // (rows laundered: the per-round offsets are added here, not kept in 2*LOADS
+      // loop-invariant registers)
+      uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
+      asm volatile("" : "+s"(rows));
+      lds_dma16(rk, vk[i & 1] + rows, ks + slot0);
+      lds_dma16(rv, vv + rows, vs + slot0);
     }
   };
 
@@ -275,16 +291,15 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // 4e+c supplies row (key) e, 4 dims at 4c of the block's 16 dims; lane i then receives
   // dim i of those 4 rows.  Lane block b16 = lane/16: half h = b16/2 selects keys 4h..4h+3
   // (of each group of 8), b16%2 selects dims 16..31 of the 32-dim block db.  The chunk of
-  // those dims sits at slot (4db + 2*(b16%2) + c/2) ^ 4e: in bytes (64db) ^ v0, v0 < 256;
-  // db = 4g + u gives voffs[u] plus an immediate 256g.
-  uint32_t voffs[4];
+  // those dims sits at slot (4db + 2*(b16%2) + c/2) ^ 4e: in bytes (64db) ^ v0, v0 < 256.
+  // With the row start (a multiple of 512) and the 8-byte half (bit 3) that is
+  // vbase ^ (64*(db%4)) + 256*(db/4): the XOR touches bits 6-7 only.
+  uint32_t vbase;
   {
     const int b16 = lane >> 4, e = (lane >> 2) & 3, c = lane & 3;
     const int h = b16 >> 1, dh = b16 & 1;
     const uint32_t v0 = static_cast<uint32_t>(16 * (2 * dh + (c >> 1)) + 64 * e);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      voffs[u] = static_cast<uint32_t>((4 * h + e) * D * 2 + (c & 1) * 8) + ((64u * u) ^ v0);
+    vbase = static_cast<uint32_t>((4 * h + e) * D * 2 + (c & 1) * 8) + v0;
   }
   const char* const smem_b = reinterpret_cast<const char*>(smem);
 
@@ -327,7 +342,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // the two transposing reads (rows +0 and +8) fetch exactly those rows of V.
   auto vfrag_load = [&](const char* vs, int s) -> u32x4 {
     const int db = s >> 1, ks16 = s & 1;
-    const char* base = vs + voffs[db & 3] + 256 * (db >> 2) + 16 * ks16 * D * 2;
+    const char* base = vs + (vbase ^ (64u * (db & 3))) + 256 * (db >> 2) + 16 * ks16 * D * 2;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
     const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * D * 2));
     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
@@ -343,7 +358,11 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     // out of the maximum and its weight exp2(c*score - m) is exactly 0.  Accumulator
     // register r of this lane holds key t*BN + 8*(r/4) + 4*hi + r%4.
     if (t == nfull) {
-      const int kvalid = Lk - t * BN - 4 * hi;
+      // (t laundered: the per-register compares must not be hoisted out of the loop as
+      // 16 loop-invariant lane masks held in scalar registers)
+      int tt = t;
+      asm volatile("" : "+s"(tt));
+      const int kvalid = Lk - tt * BN - 4 * hi;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -361,6 +380,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     const float y0 = __uint_as_float(sw2[0]), y1 = __uint_as_float(sw2[1]);
     x = NEG ? fminf(y0, y1) : fmaxf(y0, y1);
     mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
+    pin(mt[qb]);
   };
   auto check_reference = [&](int t, int it) {
     if (t == 0) {
@@ -384,7 +404,11 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       const int qb = e >> 4, r = e & 15;
       ev[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -m[qb]));
       l[qb] += ev[qb][r];
-      if (r & 1) pcur[qb][r >> 3][(r & 7) >> 1] = Elt<T>::pack2(ev[qb][r - 1], ev[qb][r]);
+      if (r & 1) {
+        uint32_t w = Elt<T>::pack2(ev[qb][r - 1], ev[qb][r]);
+        pin(w);
+        pcur[qb][r >> 3][(r & 7) >> 1] = w;
+      }
     }
   };
 
@@ -507,8 +531,8 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 
   // Epilogue: O = O^T / l (one reciprocal per row), LSE = ln2 * (m + log2 l).
   attn_agpr::fence();
-  int lane_e = lane;
-  asm volatile("" : "+v"(lane_e));  // recompute row addresses here instead of keeping them
+  // (lane index recomputed here rather than kept live across the key loop)
+  const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l[qb] + __shfl_xor(l[qb], 32);
@@ -531,7 +555,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         }
       }
     }
-    if (p.lse && hi == 0 && row < p.Lq)
+    if (p.lse && lane_e < 32 && row < p.Lq)
       p.lse[(size_t)bh * p.Lq + row] = (m[qb] + __builtin_log2f(lt)) * 0.69314718055994531f;
   }
 }
