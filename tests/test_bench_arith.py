@@ -1,0 +1,48 @@
+"""CPU checks of the benchmark's arithmetic against figures the pages print.
+
+The FLOP formula of "Xe2 ... Flash Attention -- HD=256" (section "Performance Testing")
+must reproduce the roofline percentages printed in the "Xe2 Sdp Bf16" page's performance
+table from its times, and the headline figure of the HD=256 page must be consistent with
+its stated peak (tests/golden/page_perf_figures.json, each entry with its citation).
+"""
+import json
+import os
+
+import pytest
+
+import bench
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "page_perf_figures.json")
+
+
+@pytest.fixture(scope="module")
+def figures():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def test_pages_formula_reproduces_printed_roofline(figures):
+    peak = figures["peak_tflops"]
+    for row in figures["rows"]:
+        fl = bench.flops_pages(row["q_len"], row["kv_len"], row["hd"], row["heads_q"])
+        pct = 100 * fl / (row["ms"] * 1e-3) / 1e12 / peak
+        assert abs(pct - row["roofline_pct"]) <= 0.1, (row["cite"], pct)
+
+
+def test_headline_consistent_with_peak(figures):
+    h = figures["headline"]
+    assert round(h["pct"] / 100 * figures["peak_tflops"]) == h["tflops"]
+
+
+def test_headline_formula_and_softmax_term():
+    B, Hq, Lq, Lk, D = 1, 32, 16384, 16384, 256
+    fl = bench.flops_headline(B, Hq, Lq, Lk, D)
+    assert fl == 8796093022208  # 4 * 32 * 16384^2 * 256
+    # the pages' count adds 2 flops per score for the softmax
+    assert bench.flops_pages(Lq, Lk, D, Hq, B) - fl == 2 * B * Hq * Lq * Lk
+
+
+def test_peak_is_mi355x_dense_fp16():
+    # 256 CUs x 2.4 GHz x 4096 dense fp16 flop per clock per CU
+    assert abs(bench.PEAK_TFLOPS - 2516.58) < 0.01
