@@ -95,6 +95,12 @@ struct Elt<_Float16> {
     f16x2 r = __builtin_convertvector((f32x2){x, y}, f16x2);
     return __builtin_bit_cast(uint32_t, r);
   }
+  // Row-sum update by a pair of weights x, y whose rounded values are packed in w: fp16
+  // rounding (relative 2^-11) keeps the log-sum-exp well inside its tolerance, so the sum
+  // takes the packed values in one v_dot2 with (1, 1), accumulating in fp32.
+  static __device__ __forceinline__ float sum2(uint32_t w, float, float, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), (f16x2){1, 1}, acc, false);
+  }
 };
 
 template <>
@@ -107,11 +113,15 @@ struct Elt<__bf16> {
     bf16x2 r = __builtin_convertvector((f32x2){x, y}, bf16x2);
     return __builtin_bit_cast(uint32_t, r);
   }
+  // bf16 rounding (2^-8) would move the log-sum-exp by up to ~4e-3: sum the fp32 values.
+  static __device__ __forceinline__ float sum2(uint32_t, float x, float y, float acc) {
+    return acc + (x + y);
+  }
 };
 
-// Wait states between the last MFMA writing x and any other use of x (see above).
-__device__ __forceinline__ void mfma_fence_v(f32x16& x) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
+// Wait states between the last MFMA writing x or y and any other use of them (see above).
+__device__ __forceinline__ void mfma_fence_v(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 
 // Materialise x here: the compiler may not sink its computation past this point (the
@@ -190,6 +200,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   constexpr int ROWS_PER_LOAD = attn_cfg::kThreads / CPR;  // tile rows one copy round covers
   constexpr int BM = attn_cfg::block_m(QB);
   constexpr int NSTEP = 2 * DB;  // P.V steps per tile, two MFMAs (one per query block) each
+  constexpr int VPRE = 2;        // S^T steps before the end at which the first V reads issue
   // NEG: scale < 0, so the largest scaled score comes from the smallest raw score.
   constexpr float kWorst = NEG ? __builtin_inff() : -__builtin_inff();
 
@@ -304,9 +315,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const char* const smem_b = reinterpret_cast<const char*>(smem);
 
   // Output accumulator O^T, block (qb, db) = AGPR block qb*DB + db (attn_agpr.h).
-  float m[QB], l[QB];
+  float m[QB], mk[QB], l[QB];  // mk = m + kTau, the growth threshold
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    mk[qb] = -__builtin_inff();
     m[qb] = -__builtin_inff();
     l[qb] = 0.f;
 #pragma unroll
@@ -324,10 +336,11 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // S^T(t) = K(t) Q^T, fp32 accumulation, both query blocks sharing each K fragment.  The
   // first two fragments arrive prefetched in kf[0..1]; the rest are fetched two steps ahead,
   // and the scheduling barriers keep the compiler from hoisting all of them (64 registers).
-  auto qk = [&](const char* ks, f32x16 (&sacc)[QB], u32x4 (&kf)[3]) {
+  auto qk = [&](const char* ks, f32x16 (&sacc)[QB], u32x4 (&kf)[3], auto&& tail_loads) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if (kk + 2 < KS) kf[(kk + 2) % 3] = kfrag(ks, kk + 2);
+      if (kk == KS - VPRE) tail_loads();  // first V fragments of the P.V steps
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (kk == 0) Elt<T>::mfma_v0(kf[kk % 3], qf[qb][kk], sacc[qb]);
@@ -370,31 +383,54 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
           if (8 * (r >> 2) + (r & 3) >= kvalid) sacc[qb][r] = kWorst;
     }
   };
+  // Largest scaled score: max (min for a negative scale) as a tree of depth 3 over the 16
+  // registers, so that no long chain of dependent instructions holds up the MFMA issue.
+  auto ext3 = [](float a, float b, float d) {
+    float r;
+    if constexpr (NEG) asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(d));
+    else asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(d));
+    return r;
+  };
+  auto ext2 = [](float a, float b) {
+    float r;
+    if constexpr (NEG) asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    else asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+  };
   auto row_max = [&](f32x16 (&sacc)[QB], int qb) {
-    float x = kWorst;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x = NEG ? fminf(x, sacc[qb][r]) : fmaxf(x, sacc[qb][r]);
+    const f32x16& a = sacc[qb];
+    const float m0 = ext3(a[0], a[1], a[2]), m1 = ext3(a[3], a[4], a[5]);
+    const float m2 = ext3(a[6], a[7], a[8]), m3 = ext3(a[9], a[10], a[11]);
+    const float m4 = ext3(a[12], a[13], a[14]);
+    float x = ext2(ext3(m0, m1, m2), ext3(m3, m4, a[15]));
     // the other 16 keys of this row sit in lane l^32
     const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                       false, false);
-    const float y0 = __uint_as_float(sw2[0]), y1 = __uint_as_float(sw2[1]);
-    x = NEG ? fminf(y0, y1) : fmaxf(y0, y1);
+    x = ext2(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
     mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
     pin(mt[qb]);
   };
   auto check_reference = [&](int t, int it) {
     if (t == 0) {
-      // Nothing accumulated yet: the first tile just sets the reference.
+      // Nothing accumulated yet: the first tile sets the reference (after a restart m
+      // already holds the raised value, which must be kept).
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) m[qb] = fmaxf(m[qb], mt[qb]);
+      for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = fmaxf(m[qb], mt[qb]);
+        mk[qb] = m[qb] + kTau;
+      }
     } else {
       bool grow = false;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        grow |= mt[qb] > m[qb] + kTau;
-        m[qb] = mt[qb] > m[qb] + kTau ? mt[qb] : m[qb];
+      for (int qb = 0; qb < QB; ++qb) grow |= mt[qb] > mk[qb];
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform, and rare
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          m[qb] = mt[qb] > mk[qb] ? mt[qb] : m[qb];
+          mk[qb] = m[qb] + kTau;
+        }
+        if (lane == 0) restart_flag[it & 1] = it + 1;
       }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0 && lane == 0) restart_flag[it & 1] = it + 1;
     }
   };
   float ev[QB][16];
@@ -403,10 +439,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     for (int e = e0; e < e1; ++e) {  // element e: register e%16 of query block e/16
       const int qb = e >> 4, r = e & 15;
       ev[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -m[qb]));
-      l[qb] += ev[qb][r];
       if (r & 1) {
         uint32_t w = Elt<T>::pack2(ev[qb][r - 1], ev[qb][r]);
         pin(w);
+        l[qb] = Elt<T>::sum2(w, ev[qb][r - 1], ev[qb][r], l[qb]);
         pcur[qb][r >> 3][(r & 7) >> 1] = w;
       }
     }
@@ -431,13 +467,14 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
                        u32x4 (&pcur)[QB][2]) -> bool {
     constexpr bool PV = decltype(pv_tag)::value;
     f32x16 sacc[QB];
-    qk(kstage(t), sacc, kf);
     const char* const vs = vstage(t + NSTAGE - 1);  // tile t-1
     u32x4 vf[3];
-    if constexpr (PV) {
-      vf[0] = vfrag_load(vs, 0);
-      vf[1] = vfrag_load(vs, 1);
-    }
+    qk(kstage(t), sacc, kf, [&]() {
+      if constexpr (PV) {
+        vf[0] = vfrag_load(vs, 0);
+        vf[1] = vfrag_load(vs, 1);
+      }
+    });
     int flag = 0;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
@@ -448,8 +485,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
           Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pprev[qb][s & 1]);
       }
       if (s == 0) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mfma_fence_v(sacc[qb]);
+        mfma_fence_v(sacc[0], sacc[1]);
         mask_tail(sacc, t);
         row_max(sacc, 0);
       } else if (s == 1) {
