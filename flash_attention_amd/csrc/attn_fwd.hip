@@ -180,10 +180,21 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t
                : "memory");
 }
 
-// Growth threshold, log2 units.  The exponentials use a per-row reference m fixed by the
-// first key tile; a later score may exceed m by up to kTau, so weights stay below 2^15 (fp16
-// holds up to 65504).  Exact in real arithmetic: numerator and denominator share m.
-constexpr float kTau = 15.0f;
+// Same copy with a wave-uniform extra offset soffset (added to the address, not range
+// checked): used only where every byte read lies inside the buffer.
+__device__ __forceinline__ void lds_dma16_so(i32x4 rsrc, uint32_t voffset, uint32_t soffset,
+                                             uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_dst), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory");
+}
+
+// Growth threshold.  The exponentials use a per-row reference m fixed by the first key tile;
+// as long as no lane's partial sum over a tile exceeds 2^15, no weight does either, and fp16
+// (largest value 65504) holds every weight.  Exact in real arithmetic: numerator and
+// denominator share m.
+constexpr float kGrowth = 32768.0f;
 
 template <int D, typename T, bool NEG>
 __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params p) {
@@ -256,23 +267,55 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     vv = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
   }
   const uint32_t kv_bytes = static_cast<uint32_t>(Lk) * D * 2;
-  const char* const kb = reinterpret_cast<const char*>(kh);
-  const char* const vb = reinterpret_cast<const char*>(vh);
+  // K and V base addresses of this head as wave-uniform 64-bit values (scalar registers),
+  // so that the per-tile descriptors are scalar arithmetic.
+  auto uniform64 = [](const void* ptr) {
+    const uint64_t a = reinterpret_cast<uintptr_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+  };
+  const uint64_t kb = uniform64(kh), vb = uniform64(vh);
+  // Descriptor of the buffer that starts skip bytes into K (V) and holds the rest of it,
+  // computed with scalar instructions (the compiler would otherwise use 64-bit vector adds
+  // and move the results back).
+  auto rsrc_at = [&](uint64_t base, uint32_t skip) {
+    uint32_t lo, hi, n;
+    asm("s_add_u32 %0, %3, %5\n\ts_addc_u32 %1, %4, 0\n\ts_sub_u32 %2, %6, %5"
+        : "=&s"(lo), "=&s"(hi), "=&s"(n)
+        : "s"(static_cast<uint32_t>(base)), "s"(static_cast<uint32_t>(base >> 32)),
+          "s"(__builtin_amdgcn_readfirstlane(skip)), "s"(kv_bytes)
+        : "scc");
+    return (i32x4){static_cast<int>(lo), static_cast<int>(hi), static_cast<int>(n), 0x00020000};
+  };
   auto issue_tile = [&](int t, int st) {
     const uint32_t ks = lds_base + static_cast<uint32_t>(st * 4 * TILE);
     const uint32_t vs = ks + 2 * TILE;
     const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // t < ntiles: skip < kv_bytes
-    const i32x4 rk = make_rsrc(kb + skip, kv_bytes - skip);
-    const i32x4 rv = make_rsrc(vb + skip, kv_bytes - skip);
+    const i32x4 rk = rsrc_at(kb, skip);
+    const i32x4 rv = rsrc_at(vb, skip);
+    if (t < nfull) {
+      // All 32 rows exist: the per-round row offset goes into the scalar offset and every
+      // copy uses the lane's fixed offset (no vector arithmetic, no reuse of one register).
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const uint32_t slot0 = (i * attn_cfg::kThreads + wave * 64) * 16;  // wave-uniform
-      // (rows laundered: the per-round offsets are added here, not kept in 2*LOADS
-      // loop-invariant registers)
-      uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
-      asm volatile("" : "+s"(rows));
-      lds_dma16(rk, vk[i & 1] + rows, ks + slot0);
-      lds_dma16(rv, vv + rows, vs + slot0);
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t slot0 = (i * attn_cfg::kThreads + wave * 64) * 16;  // wave-uniform
+        const uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
+        lds_dma16_so(rk, vk[i & 1], rows, ks + slot0);
+        lds_dma16_so(rv, vv, rows, vs + slot0);
+      }
+    } else {
+      // The partial last tile: rows past Lk must fall outside the buffer and read as zero,
+      // so the row offset goes into the range-checked per-lane offset.
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t slot0 = (i * attn_cfg::kThreads + wave * 64) * 16;
+        // (rows laundered: added here, not hoisted into loop-invariant registers)
+        uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
+        asm volatile("" : "+s"(rows));
+        lds_dma16(rk, vk[i & 1] + rows, ks + slot0);
+        lds_dma16(rv, vv + rows, vs + slot0);
+      }
     }
   };
 
@@ -290,7 +333,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 
   issue_tile(0, 0);
   if (ntiles > 1) issue_tile(1, 1);
-  if (tid < 2) restart_flag[tid] = 0;  // 0 never matches an iteration number (read at it >= 1)
+  if (tid < 2) restart_flag[tid] = -1;  // never an iteration number
 
   // ---- per-lane LDS byte offsets of the fragment reads (stage base added later) ----
   // K (A operand of S^T): row l%32, chunk 2kk+hi at slot (2kk+hi) ^ sw, sw = swz_k(l%32);
@@ -315,10 +358,9 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const char* const smem_b = reinterpret_cast<const char*>(smem);
 
   // Output accumulator O^T, block (qb, db) = AGPR block qb*DB + db (attn_agpr.h).
-  float m[QB], mk[QB], l[QB];  // mk = m + kTau, the growth threshold
+  float m[QB], l[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    mk[qb] = -__builtin_inff();
     m[qb] = -__builtin_inff();
     l[qb] = 0.f;
 #pragma unroll
@@ -410,30 +452,13 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
     pin(mt[qb]);
   };
-  auto check_reference = [&](int t, int it) {
-    if (t == 0) {
-      // Nothing accumulated yet: the first tile sets the reference (after a restart m
-      // already holds the raised value, which must be kept).
+  // The first tile fixes the reference: m = its row maximum (or the exact maximum found
+  // by a restart's maximum sweep, which is never smaller).
+  auto set_reference = [&]() {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        m[qb] = fmaxf(m[qb], mt[qb]);
-        mk[qb] = m[qb] + kTau;
-      }
-    } else {
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) grow |= mt[qb] > mk[qb];
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform, and rare
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          m[qb] = mt[qb] > mk[qb] ? mt[qb] : m[qb];
-          mk[qb] = m[qb] + kTau;
-        }
-        if (lane == 0) restart_flag[it & 1] = it + 1;
-      }
-    }
+    for (int qb = 0; qb < QB; ++qb) m[qb] = fmaxf(m[qb], mt[qb]);
   };
-  float ev[QB][16];
+  float ev[QB][16], lt[QB];
   auto exp_slice = [&](f32x16 (&sacc)[QB], u32x4 (&pcur)[QB][2], int e0, int e1) {
 #pragma unroll
     for (int e = e0; e < e1; ++e) {  // element e: register e%16 of query block e/16
@@ -442,19 +467,39 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       if (r & 1) {
         uint32_t w = Elt<T>::pack2(ev[qb][r - 1], ev[qb][r]);
         pin(w);
-        l[qb] = Elt<T>::sum2(w, ev[qb][r - 1], ev[qb][r], l[qb]);
+        // this tile's part of the row sum (lane-local 16 keys)
+        lt[qb] = Elt<T>::sum2(w, ev[qb][r - 1], ev[qb][r], r == 1 ? 0.f : lt[qb]);
         pcur[qb][r >> 3][(r & 7) >> 1] = w;
       }
     }
   };
+  // Growth check of tile t >= 1, after its exponentials: a weight above kGrowth (the scores
+  // outgrew the reference) shows up as a lane's partial tile sum above kGrowth, since all
+  // weights are non-negative.  Such a tile raises a restart flag, seen at the next
+  // synchronisation point.  After a restart m holds the exact maxima (no weight exceeds 1)
+  // and the check is off, so a sweep restarts at most once whatever the data.
+  bool exact_m = false;
+  auto check_growth = [&](int it) {
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) grow |= lt[qb] > kGrowth;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0 && !exact_m) {  // uniform, and rare
+      if (lane == 0) restart_flag[it & 1] = it + 1;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the flag is in LDS before any barrier
+    }
+  };
 
-  // Synchronisation point of iteration t (in the middle of its P.V steps): tile t+1 has
-  // landed everywhere, every wave is past iteration t-1 so the stage of tile t-2 can take
-  // tile t+2, and the restart flags written before it are visible.
+  // Synchronisation point of iteration it (tile t, near the end of its P.V steps): tile t+1
+  // has landed everywhere, every wave is past iteration it-1 (so the stage of tile t-2 can
+  // take tile t+2) and any restart flag raised at the end of iteration it-1 is visible.
   auto sync_point = [&](int t, int it) -> int {
     if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of tile t+1
-    __syncthreads();
-    const int flag = restart_flag[it & 1];  // consumed at the end of the iteration
+    // A bare s_barrier: the LDS reads still in flight here (V fragments of tile t-1) touch
+    // no stage that is about to be overwritten, so they need not complete first.  The only
+    // LDS write another wave reads after this barrier is a restart flag, whose writer waits
+    // for it before arriving.
+    __builtin_amdgcn_s_barrier();
+    const int flag = restart_flag[(it + 1) & 1];  // raised by iteration it-1 as value it
     if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
     return flag;
   };
@@ -475,7 +520,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         vf[1] = vfrag_load(vs, 1);
       }
     });
-    int flag = 0;
+    int flag = -1;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if constexpr (PV) {
@@ -487,24 +532,29 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       if (s == 0) {
         mfma_fence_v(sacc[0], sacc[1]);
         mask_tail(sacc, t);
-        row_max(sacc, 0);
+        if (!PV) row_max(sacc, 0);  // tile 0 only: it fixes the reference
       } else if (s == 1) {
-        row_max(sacc, 1);
+        if (!PV) row_max(sacc, 1);
       } else if (s == 2) {
-        check_reference(t, it);
+        if (!PV) set_reference();
       } else {
         // the 32 exponentials spread over steps 3..NSTEP-1
         exp_slice(sacc, pcur, 32 * (s - 3) / (NSTEP - 3), 32 * (s - 2) / (NSTEP - 3));
       }
       if (s == SYNC_STEP) flag = sync_point(t, it);
-      if (s == NSTEP - 1 && t + 1 < ntiles) {
-        // first two K fragments of tile t+1 (landed at the sync point)
-        kf[0] = kfrag(kstage(t + 1), 0);
-        kf[1] = kfrag(kstage(t + 1), 1);
+      if (s == NSTEP - 1) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
+        if (PV) check_growth(it);
+        if (t + 1 < ntiles) {
+          // first two K fragments of tile t+1 (landed at the sync point)
+          kf[0] = kfrag(kstage(t + 1), 0);
+          kf[1] = kfrag(kstage(t + 1), 1);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return __builtin_amdgcn_readfirstlane(flag) == it + 1;
+    return __builtin_amdgcn_readfirstlane(flag) == it;
   };
   // P.V of the last tile (no softmax, no synchronisation).
   auto drain = [&](int t, u32x4 (&pprev)[QB][2]) {
@@ -521,16 +571,44 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Exact row maxima over all key tiles (S^T products only), for a restart: afterwards no
+  // weight exceeds 1 and no tile can trigger another restart.  Uses the same stages and
+  // copies as the main sweep; every stage is idle on entry and on exit.
+  auto max_sweep = [&]() {
+    issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m[qb] = kWorst * c;  // -inf in scaled units
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 1 < ntiles) WAIT_VMCNT(2 * LOADS);  // tile t landed (tile t+1 may not have)
+      else WAIT_VMCNT(0);
+      __syncthreads();  // tile t visible; every wave is done with tile t-2's stage
+      if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
+      kf[0] = kfrag(kstage(t), 0);
+      kf[1] = kfrag(kstage(t), 1);
+      f32x16 sacc[QB];
+      qk(kstage(t), sacc, kf, [] {});
+      mfma_fence_v(sacc[0], sacc[1]);
+      mask_tail(sacc, t);
+      row_max(sacc, 0);
+      row_max(sacc, 1);
+      set_reference();
+    }
+    WAIT_VMCNT(0);
+    __syncthreads();  // nobody reads a stage any more
+  };
 
   // ---- the key loop ----
   // `it` counts iterations including restarts and never resets, so a restart flag written
-  // in one iteration cannot be mistaken for another's.  Restart: a wave whose row maximum
-  // outgrew its reference m by more than kTau raised m and flagged it before the sync
-  // point; at the end of that iteration every wave starts the key sweep over with zeroed
-  // accumulators (the references stay valid).  This replaces the usual per-tile rescale of
-  // the output accumulator by exp2(m_old - m_new): the accumulator is only ever written by
-  // MFMAs, and with the first tile fixing m a restart needs the scores to grow by more than
-  // 2^kTau.  The loop is unrolled by two so the P buffers swap roles without copies.
+  // in one iteration cannot be mistaken for another's.  The weights use a per-row reference
+  // m fixed by the first key tile instead of the usual running maximum, so the output
+  // accumulator is never rescaled (it is only ever written by MFMAs).  If a later tile
+  // outgrows m by more than kTau (rare: the scores must grow by a factor 2^kTau), the tile
+  // raises a flag; at the end of the next iteration (or before the last tile's P.V product)
+  // every wave stops, a maximum sweep finds the exact row maxima, and the key sweep starts
+  // over with zeroed accumulators.  Exact in real arithmetic for any m: numerator and
+  // denominator share it.  The loop is unrolled by two so the P buffers swap roles without
+  // copies.
   u32x4 pa[QB][2], pb2[QB][2];
   int it = 0;
   for (;;) {
@@ -549,12 +627,20 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       ++t;
     }
     if (!restart) {
+      // a flag raised by the last iteration (counter it-1) has had no sync point yet
+      __builtin_amdgcn_s_barrier();
+      restart = __builtin_amdgcn_readfirstlane(restart_flag[(it - 1) & 1]) == it;
+    }
+    if (!restart) {
       if (ntiles & 1) drain(ntiles - 1, pa);  // P(t) lives in pa for even t
       else drain(ntiles - 1, pb2);
       break;
     }
     WAIT_VMCNT(0);
-    __syncthreads();  // nobody still reads a stage
+    if (tid < 2) restart_flag[tid] = -1;  // flags of the abandoned sweep
+    __syncthreads();  // nobody still reads a stage or a flag
+    max_sweep();
+    exact_m = true;
     issue_tile(0, 0);
     if (ntiles > 1) issue_tile(1, 1);
 #pragma unroll
