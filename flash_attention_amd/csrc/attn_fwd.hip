@@ -289,8 +289,8 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     return (i32x4){static_cast<int>(lo), static_cast<int>(hi), static_cast<int>(n), 0x00020000};
   };
   auto issue_tile = [&](int t, int st) {
-    const uint32_t ks = lds_base + static_cast<uint32_t>(st * 4 * TILE);
-    const uint32_t vs = ks + 2 * TILE;
+    const uint32_t ks = lds_base + static_cast<uint32_t>(st * 2 * TILE);
+    const uint32_t vs = ks + NSTAGE * 2 * TILE;
     const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // t < ntiles: skip < kv_bytes
     const i32x4 rk = rsrc_at(kb, skip);
     const i32x4 rv = rsrc_at(vb, skip);
@@ -369,8 +369,11 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const float c = p.c;
 
   // ---- building blocks of one key-loop iteration ----
-  auto kstage = [&](int t) { return smem_b + (t % NSTAGE) * 4 * TILE; };
-  auto vstage = [&](int t) { return smem_b + (t % NSTAGE) * 4 * TILE + TILE * 2; };
+  // LDS: the K tiles of the four stages, then their V tiles.  Both rings lie within 64 KiB
+  // of their base, so with the stage known at compile time the stage offset is the
+  // immediate offset of the LDS reads (no address arithmetic in the loop).
+  auto kstage = [&](int st) { return smem_b + st * 2 * TILE; };
+  auto vstage = [&](int st) { return smem_b + (NSTAGE + st) * 2 * TILE; };
   // K fragment kk of a tile: the A operand of S^T step kk.
   auto kfrag = [&](const char* ks, int kk) {
     return *reinterpret_cast<const u32x4*>(ks + krow + ((32u * kk) ^ k0));
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // Synchronisation point of iteration it (tile t, near the end of its P.V steps): tile t+1
   // has landed everywhere, every wave is past iteration it-1 (so the stage of tile t-2 can
   // take tile t+2) and any restart flag raised at the end of iteration it-1 is visible.
-  auto sync_point = [&](int t, int it) -> int {
+  auto sync_point = [&](int t, int st, int it) -> int {
     if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of tile t+1
     // A bare s_barrier: the LDS reads still in flight here (V fragments of tile t-1) touch
     // no stage that is about to be overwritten, so they need not complete first.  The only
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     // for it before arriving.
     __builtin_amdgcn_s_barrier();
     const int flag = restart_flag[(it + 1) & 1];  // raised by iteration it-1 as value it
-    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
+    if (t + 2 < ntiles) issue_tile(t + 2, (st + 2) % NSTAGE);
     return flag;
   };
 
@@ -508,13 +511,15 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // (PV) with the softmax of tile t in slices underneath.  Returns true for a restart.
   constexpr int SYNC_STEP = NSTEP - 3;  // two P.V steps remain after the sync point
   u32x4 kf[3];
-  auto iteration = [&](auto pv_tag, int t, int it, u32x4 (&pprev)[QB][2],
+  // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
+  auto iteration = [&](auto pv_tag, auto st_tag, int t, int it, u32x4 (&pprev)[QB][2],
                        u32x4 (&pcur)[QB][2]) -> bool {
     constexpr bool PV = decltype(pv_tag)::value;
+    constexpr int ST = decltype(st_tag)::value;
     f32x16 sacc[QB];
-    const char* const vs = vstage(t + NSTAGE - 1);  // tile t-1
+    const char* const vs = vstage((ST + NSTAGE - 1) % NSTAGE);  // tile t-1
     u32x4 vf[3];
-    qk(kstage(t), sacc, kf, [&]() {
+    qk(kstage(ST), sacc, kf, [&]() {
       if constexpr (PV) {
         vf[0] = vfrag_load(vs, 0);
         vf[1] = vfrag_load(vs, 1);
@@ -541,15 +546,15 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         // the 32 exponentials spread over steps 3..NSTEP-1
         exp_slice(sacc, pcur, 32 * (s - 3) / (NSTEP - 3), 32 * (s - 2) / (NSTEP - 3));
       }
-      if (s == SYNC_STEP) flag = sync_point(t, it);
+      if (s == SYNC_STEP) flag = sync_point(t, ST, it);
       if (s == NSTEP - 1) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
         if (PV) check_growth(it);
         if (t + 1 < ntiles) {
           // first two K fragments of tile t+1 (landed at the sync point)
-          kf[0] = kfrag(kstage(t + 1), 0);
-          kf[1] = kfrag(kstage(t + 1), 1);
+          kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
+          kf[1] = kfrag(kstage((ST + 1) % NSTAGE), 1);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   };
   // P.V of the last tile (no softmax, no synchronisation).
   auto drain = [&](int t, u32x4 (&pprev)[QB][2]) {
-    const char* const vs = vstage(t);
+    const char* const vs = vstage(t % NSTAGE);
     u32x4 vf[3];
     vf[0] = vfrag_load(vs, 0);
     vf[1] = vfrag_load(vs, 1);
@@ -584,10 +589,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       else WAIT_VMCNT(0);
       __syncthreads();  // tile t visible; every wave is done with tile t-2's stage
       if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
-      kf[0] = kfrag(kstage(t), 0);
-      kf[1] = kfrag(kstage(t), 1);
+      kf[0] = kfrag(kstage(t % NSTAGE), 0);
+      kf[1] = kfrag(kstage(t % NSTAGE), 1);
       f32x16 sacc[QB];
-      qk(kstage(t), sacc, kf, [] {});
+      qk(kstage(t % NSTAGE), sacc, kf, [] {});
       mfma_fence_v(sacc[0], sacc[1]);
       mask_tail(sacc, t);
       row_max(sacc, 0);
@@ -607,8 +612,8 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // raises a flag; at the end of the next iteration (or before the last tile's P.V product)
   // every wave stops, a maximum sweep finds the exact row maxima, and the key sweep starts
   // over with zeroed accumulators.  Exact in real arithmetic for any m: numerator and
-  // denominator share it.  The loop is unrolled by two so the P buffers swap roles without
-  // copies.
+  // denominator share it.  The loop is unrolled by four: the stage of each iteration is a
+  // compile-time constant and the two P buffers swap roles without copies.
   u32x4 pa[QB][2], pb2[QB][2];
   int it = 0;
   for (;;) {
@@ -617,13 +622,20 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     __syncthreads();
     kf[0] = kfrag(kstage(0), 0);
     kf[1] = kfrag(kstage(0), 1);
-    bool restart = iteration(std::false_type{}, 0, it++, pb2, pa);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    bool restart = iteration(std::false_type{}, S0{}, 0, it++, pb2, pa);
     int t = 1;
-    while (!restart && t < ntiles) {
-      restart = iteration(std::true_type{}, t, it++, pa, pb2);  // P(t-1) in pa
-      ++t;
-      if (restart || t >= ntiles) break;
-      restart = iteration(std::true_type{}, t, it++, pb2, pa);  // P(t-1) in pb2
+    while (!restart && t < ntiles) {  // P(t-1) in pa for odd t, in pb2 for even t
+      restart = iteration(std::true_type{}, S1{}, t, it++, pa, pb2);
+      if (restart || ++t >= ntiles) break;
+      restart = iteration(std::true_type{}, S2{}, t, it++, pb2, pa);
+      if (restart || ++t >= ntiles) break;
+      restart = iteration(std::true_type{}, S3{}, t, it++, pa, pb2);
+      if (restart || ++t >= ntiles) break;
+      restart = iteration(std::true_type{}, S0{}, t, it++, pb2, pa);
       ++t;
     }
     if (!restart) {
