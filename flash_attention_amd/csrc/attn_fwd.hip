@@ -289,7 +289,9 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     return (i32x4){static_cast<int>(lo), static_cast<int>(hi), static_cast<int>(n), 0x00020000};
   };
   auto issue_tile = [&](int t, int st) {
-    const uint32_t ks = lds_base + static_cast<uint32_t>(st * 2 * TILE);
+    // (laundered: the destinations are added here, not kept per stage in scalar registers)
+    uint32_t ks = lds_base + static_cast<uint32_t>(st * 2 * TILE);
+    asm volatile("" : "+s"(ks));
     const uint32_t vs = ks + NSTAGE * 2 * TILE;
     const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // t < ntiles: skip < kv_bytes
     const i32x4 rk = rsrc_at(kb, skip);
@@ -369,11 +371,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const float c = p.c;
 
   // ---- building blocks of one key-loop iteration ----
-  // LDS: the K tiles of the four stages, then their V tiles.  Both rings lie within 64 KiB
-  // of their base, so with the stage known at compile time the stage offset is the
-  // immediate offset of the LDS reads (no address arithmetic in the loop).
+  // LDS: the K tiles of the four stages, then their V tiles.  Each ring spans at most
+  // 64 KiB, so with the stage known at compile time the stage offset is the immediate
+  // offset of the LDS reads (no address arithmetic in the loop).
   auto kstage = [&](int st) { return smem_b + st * 2 * TILE; };
-  auto vstage = [&](int st) { return smem_b + (NSTAGE + st) * 2 * TILE; };
   // K fragment kk of a tile: the A operand of S^T step kk.
   auto kfrag = [&](const char* ks, int kk) {
     return *reinterpret_cast<const u32x4*>(ks + krow + ((32u * kk) ^ k0));
@@ -398,11 +399,21 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // P^T blocks.  MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator
   // registers 8ks..8ks+7, whose keys for lane half h are 16ks + {4h..4h+3, 8+4h..8+4h+3}:
   // the two transposing reads (rows +0 and +8) fetch exactly those rows of V.
-  auto vfrag_load = [&](const char* vs, int s) -> u32x4 {
+  // Per-lane LDS byte addresses of V fragment group j = db % 4 in stage 0 of the V ring
+  // (laundered, so that the stage and the remaining offsets stay immediate offsets of the
+  // reads instead of being folded into per-stage address registers).
+  uint32_t vlane[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vlane[j] = lds_base + NSTAGE * 2 * TILE + (vbase ^ (64u * j));
+    asm volatile("" : "+v"(vlane[j]));
+  }
+  auto vfrag_load = [&](int st, int s) -> u32x4 {
     const int db = s >> 1, ks16 = s & 1;
-    const char* base = vs + (vbase ^ (64u * (db & 3))) + 256 * (db >> 2) + 16 * ks16 * D * 2;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * D * 2));
+    const uint32_t base = vlane[db & 3] + st * 2 * TILE + 256 * (db >> 2) + 16 * ks16 * D * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base));
+    const s16x4 up =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + 8 * D * 2));
     const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
     return (u32x4){lo2[0], lo2[1], up2[0], up2[1]};
   };
@@ -517,19 +528,19 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
     f32x16 sacc[QB];
-    const char* const vs = vstage((ST + NSTAGE - 1) % NSTAGE);  // tile t-1
+    constexpr int VST = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
     u32x4 vf[3];
     qk(kstage(ST), sacc, kf, [&]() {
       if constexpr (PV) {
-        vf[0] = vfrag_load(vs, 0);
-        vf[1] = vfrag_load(vs, 1);
+        vf[0] = vfrag_load(VST, 0);
+        vf[1] = vfrag_load(VST, 1);
       }
     });
     int flag = -1;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if constexpr (PV) {
-        if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(vs, s + 2);
+        if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(VST, s + 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pprev[qb][s & 1]);
@@ -563,13 +574,13 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   };
   // P.V of the last tile (no softmax, no synchronisation).
   auto drain = [&](int t, u32x4 (&pprev)[QB][2]) {
-    const char* const vs = vstage(t % NSTAGE);
+    const int st = t % NSTAGE;
     u32x4 vf[3];
-    vf[0] = vfrag_load(vs, 0);
-    vf[1] = vfrag_load(vs, 1);
+    vf[0] = vfrag_load(st, 0);
+    vf[1] = vfrag_load(st, 1);
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(vs, s + 2);
+      if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(st, s + 2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pprev[qb][s & 1]);
