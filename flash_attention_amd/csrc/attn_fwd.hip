@@ -505,7 +505,8 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 
   // Synchronisation point of iteration it (tile t, near the end of its P.V steps): tile t+1
   // has landed everywhere, every wave is past iteration it-1 (so the stage of tile t-2 can
-  // take tile t+2) and any restart flag raised at the end of iteration it-1 is visible.
+  // take tile t+2, copied in the steps after this point) and any restart flag raised at the
+  // end of iteration it-1 is visible.
   auto sync_point = [&](int t, int st, int it) -> int {
     if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of tile t+1
     // A bare s_barrier: the LDS reads still in flight here (V fragments of tile t-1) touch
@@ -514,13 +515,12 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     // for it before arriving.
     __builtin_amdgcn_s_barrier();
     const int flag = restart_flag[(it + 1) & 1];  // raised by iteration it-1 as value it
-    if (t + 2 < ntiles) issue_tile(t + 2, (st + 2) % NSTAGE);
     return flag;
   };
 
   // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
   // (PV) with the softmax of tile t in slices underneath.  Returns true for a restart.
-  constexpr int SYNC_STEP = NSTEP - 3;  // two P.V steps remain after the sync point
+  constexpr int SYNC_STEP = NSTEP - 4;  // three P.V steps remain after the sync point
   u32x4 kf[3];
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
   auto iteration = [&](auto pv_tag, auto st_tag, int t, int it, u32x4 (&pprev)[QB][2],
@@ -558,6 +558,11 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         exp_slice(sacc, pcur, 32 * (s - 3) / (NSTEP - 3), 32 * (s - 2) / (NSTEP - 3));
       }
       if (s == SYNC_STEP) flag = sync_point(t, ST, it);
+      // copies of tile t+2, one wave per step after the synchronisation point, so that the
+      // four waves' copies do not queue up behind each other
+      static_assert(SYNC_STEP + attn_cfg::kWaves == NSTEP, "one copy step per wave");
+      if (s >= SYNC_STEP && t + 2 < ntiles && wave == s - SYNC_STEP)
+        issue_tile(t + 2, (ST + 2) % NSTAGE);
       if (s == NSTEP - 1) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
