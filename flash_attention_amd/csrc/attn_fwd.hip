@@ -68,8 +68,9 @@ struct Params {
 // written far earlier, so no wait states precede the MFMAs (each s_nop in front of one
 // costs about a tenth of the matrix-core rate); tests/test_kernel_asm.py checks on the
 // emitted code that no VALU write lands within 2 wait states of an MFMA reading it.  Every
-// VALU reader of an MFMA result is ordered behind a fence of 24 wait states (an 8-pass XDL
-// result needs NumPasses + 3), also checked there.
+// VALU reader of an MFMA result is ordered behind a fence of 12 wait states (what the
+// compiler's own hazard recognizer puts between this 8-pass MFMA and a VALU read on gfx950),
+// also checked there.
 #define ATTN_MFMA_F16 "v_mfma_f32_32x32x16_f16"
 #define ATTN_MFMA_BF16 "v_mfma_f32_32x32x16_bf16"
 #define ATTN_MFMA_STMTS(OPC)                                                              \
@@ -121,7 +122,7 @@ struct Elt<__bf16> {
 
 // Wait states between the last MFMA writing x or y and any other use of them (see above).
 __device__ __forceinline__ void mfma_fence_v(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+  asm volatile("s_nop 11" : "+v"(x), "+v"(y));
 }
 
 // Materialise x here: the compiler may not sink its computation past this point (the
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 
   extern __shared__ u32x4 smem_raw[];
   uint16_t* const smem = reinterpret_cast<uint16_t*>(smem_raw);
-  // Two restart flags after the K/V stages (written by at most one lane per wave), read
+  // The restart flag after the K/V stages (written by at most one lane per wave), read
   // through an LDS pointer so the read waits on LDS traffic only.
   typedef __attribute__((address_space(3))) volatile int lds_vint;
   lds_vint* const restart_flag = (lds_vint*)(smem + NSTAGE * 2 * TILE);
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 
   issue_tile(0, 0);
   if (ntiles > 1) issue_tile(1, 1);
-  if (tid < 2) restart_flag[tid] = -1;  // never an iteration number
+  if (tid == 0) restart_flag[0] = 0;
 
   // ---- per-lane LDS byte offsets of the fragment reads (stage base added later) ----
   // K (A operand of S^T): row l%32, chunk 2kk+hi at slot (2kk+hi) ^ sw, sw = swz_k(l%32);
@@ -489,42 +490,34 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   };
   // Growth check of tile t >= 1, after its exponentials: a weight above kGrowth (the scores
   // outgrew the reference) shows up as a lane's partial tile sum above kGrowth, since all
-  // weights are non-negative.  Such a tile raises a restart flag, seen at the next
-  // synchronisation point.  After a restart m holds the exact maxima (no weight exceeds 1)
-  // and the check is off, so a sweep restarts at most once whatever the data.
-  bool exact_m = false;
-  auto check_growth = [&](int it) {
+  // weights are non-negative.  The wave remembers it; the workgroup looks once, at the end
+  // of the sweep.  After a restart m holds the exact maxima (no weight exceeds 1) and the
+  // check is off, so a sweep restarts at most once whatever the data.
+  bool exact_m = false, grew = false;
+  auto check_growth = [&]() {
     bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) grow |= lt[qb] > kGrowth;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0 && !exact_m) {  // uniform, and rare
-      if (lane == 0) restart_flag[it & 1] = it + 1;
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the flag is in LDS before any barrier
-    }
+    grew |= __builtin_amdgcn_ballot_w64(grow) != 0;  // wave-uniform
   };
 
-  // Synchronisation point of iteration it (tile t, near the end of its P.V steps): tile t+1
-  // has landed everywhere, every wave is past iteration it-1 (so the stage of tile t-2 can
-  // take tile t+2, copied in the steps after this point) and any restart flag raised at the
-  // end of iteration it-1 is visible.
-  auto sync_point = [&](int t, int st, int it) -> int {
+  // Synchronisation point of iteration t (near the end of its P.V steps): tile t+1 has
+  // landed everywhere and every wave is past iteration t-1, so the stage of tile t-2 can take
+  // tile t+2, copied in the steps after this point.
+  auto sync_point = [&](int t) {
     if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of tile t+1
     // A bare s_barrier: the LDS reads still in flight here (V fragments of tile t-1) touch
-    // no stage that is about to be overwritten, so they need not complete first.  The only
-    // LDS write another wave reads after this barrier is a restart flag, whose writer waits
-    // for it before arriving.
+    // no stage that is about to be overwritten, so they need not complete first.
     __builtin_amdgcn_s_barrier();
-    const int flag = restart_flag[(it + 1) & 1];  // raised by iteration it-1 as value it
-    return flag;
   };
 
   // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
-  // (PV) with the softmax of tile t in slices underneath.  Returns true for a restart.
+  // (PV) with the softmax of tile t in slices underneath.
   constexpr int SYNC_STEP = NSTEP - 4;  // three P.V steps remain after the sync point
   u32x4 kf[3];
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
-  auto iteration = [&](auto pv_tag, auto st_tag, int t, int it, u32x4 (&pprev)[QB][2],
-                       u32x4 (&pcur)[QB][2]) -> bool {
+  auto iteration = [&](auto pv_tag, auto st_tag, int t, u32x4 (&pprev)[QB][2],
+                       u32x4 (&pcur)[QB][2]) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
     f32x16 sacc[QB];
@@ -536,7 +529,6 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         vf[1] = vfrag_load(VST, 1);
       }
     });
-    int flag = -1;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if constexpr (PV) {
@@ -557,7 +549,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         // the 32 exponentials spread over steps 3..NSTEP-1
         exp_slice(sacc, pcur, 32 * (s - 3) / (NSTEP - 3), 32 * (s - 2) / (NSTEP - 3));
       }
-      if (s == SYNC_STEP) flag = sync_point(t, ST, it);
+      if (s == SYNC_STEP) sync_point(t);
       // copies of tile t+2, one wave per step after the synchronisation point, so that the
       // four waves' copies do not queue up behind each other
       static_assert(SYNC_STEP + attn_cfg::kWaves == NSTEP, "one copy step per wave");
@@ -566,7 +558,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       if (s == NSTEP - 1) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
-        if (PV) check_growth(it);
+        if (PV && !exact_m) check_growth();
         if (t + 1 < ntiles) {
           // first two K fragments of tile t+1 (landed at the sync point)
           kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
@@ -575,7 +567,6 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return __builtin_amdgcn_readfirstlane(flag) == it;
   };
   // P.V of the last tile (no softmax, no synchronisation).
   auto drain = [&](int t, u32x4 (&pprev)[QB][2]) {
@@ -620,18 +611,15 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   };
 
   // ---- the key loop ----
-  // `it` counts iterations including restarts and never resets, so a restart flag written
-  // in one iteration cannot be mistaken for another's.  The weights use a per-row reference
-  // m fixed by the first key tile instead of the usual running maximum, so the output
-  // accumulator is never rescaled (it is only ever written by MFMAs).  If a later tile
-  // outgrows m by more than kTau (rare: the scores must grow by a factor 2^kTau), the tile
-  // raises a flag; at the end of the next iteration (or before the last tile's P.V product)
-  // every wave stops, a maximum sweep finds the exact row maxima, and the key sweep starts
-  // over with zeroed accumulators.  Exact in real arithmetic for any m: numerator and
-  // denominator share it.  The loop is unrolled by four: the stage of each iteration is a
-  // compile-time constant and the two P buffers swap roles without copies.
+  // The weights use a per-row reference m fixed by the first key tile instead of the usual
+  // running maximum, so the output accumulator is never rescaled (it is only ever written
+  // by MFMAs).  If a later tile outgrows m by more than a factor kGrowth (rare: the scores
+  // must grow by 15 in log2 units), the sweep's results are discarded: a maximum sweep finds
+  // the exact row maxima and the key sweep starts over with zeroed accumulators.  Exact in
+  // real arithmetic for any m: numerator and denominator share it.  The loop is unrolled by
+  // four: the stage of each iteration is a compile-time constant and the two P buffers
+  // swap roles without copies.
   u32x4 pa[QB][2], pb2[QB][2];
-  int it = 0;
   for (;;) {
     if (ntiles > 1) WAIT_VMCNT(2 * LOADS);  // tile 0 landed (tile 1 may be in flight)
     else WAIT_VMCNT(0);
@@ -642,33 +630,36 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
-    bool restart = iteration(std::false_type{}, S0{}, 0, it++, pb2, pa);
+    iteration(std::false_type{}, S0{}, 0, pb2, pa);
     int t = 1;
-    while (!restart && t < ntiles) {  // P(t-1) in pa for odd t, in pb2 for even t
-      restart = iteration(std::true_type{}, S1{}, t, it++, pa, pb2);
-      if (restart || ++t >= ntiles) break;
-      restart = iteration(std::true_type{}, S2{}, t, it++, pb2, pa);
-      if (restart || ++t >= ntiles) break;
-      restart = iteration(std::true_type{}, S3{}, t, it++, pa, pb2);
-      if (restart || ++t >= ntiles) break;
-      restart = iteration(std::true_type{}, S0{}, t, it++, pb2, pa);
+    while (t < ntiles) {  // P(t-1) in pa for odd t, in pb2 for even t
+      iteration(std::true_type{}, S1{}, t, pa, pb2);
+      if (++t >= ntiles) break;
+      iteration(std::true_type{}, S2{}, t, pb2, pa);
+      if (++t >= ntiles) break;
+      iteration(std::true_type{}, S3{}, t, pa, pb2);
+      if (++t >= ntiles) break;
+      iteration(std::true_type{}, S0{}, t, pb2, pa);
       ++t;
     }
-    if (!restart) {
-      // a flag raised by the last iteration (counter it-1) has had no sync point yet
-      __builtin_amdgcn_s_barrier();
-      restart = __builtin_amdgcn_readfirstlane(restart_flag[(it - 1) & 1]) == it;
+    // Did any wave see its scores outgrow the reference?  (The writer waits for its flag
+    // before the barrier; every wave reads it before the next barrier.)
+    if (grew) {
+      if (lane == 0) restart_flag[0] = 1;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     }
-    if (!restart) {
+    __builtin_amdgcn_s_barrier();
+    if (__builtin_amdgcn_readfirstlane(restart_flag[0]) == 0) {
       if (ntiles & 1) drain(ntiles - 1, pa);  // P(t) lives in pa for even t
       else drain(ntiles - 1, pb2);
       break;
     }
     WAIT_VMCNT(0);
-    if (tid < 2) restart_flag[tid] = -1;  // flags of the abandoned sweep
-    __syncthreads();  // nobody still reads a stage or a flag
+    __syncthreads();  // nobody still reads a stage or the flag
+    if (tid == 0) restart_flag[0] = 0;  // (ordered by the barriers of the maximum sweep)
     max_sweep();
-    exact_m = true;
+    exact_m = true;  // no further growth checks: no wave can set grew again
+    grew = false;
     issue_tile(0, 0);
     if (ntiles > 1) issue_tile(1, 1);
 #pragma unroll

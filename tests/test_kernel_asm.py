@@ -78,9 +78,11 @@ def test_no_packed_fp32(asm):
 # ---- MFMA hazard check ------------------------------------------------------------------
 # The MFMAs are inline asm, so the compiler inserts no wait states around them.  The ISA
 # requires (gfx940 family): 2 wait states between a VALU write of a VGPR and an MFMA reading
-# it, and NumPasses + 3 between an MFMA writing a register and a VALU access to it (11 for
-# the 8-pass 32x32x16 ops; 18 is checked here).  MFMA -> MFMA accumulation into the same
-# registers is interlocked by the hardware.  These checks walk the emitted code.
+# it, and between an MFMA writing a register and a VALU access to it the 12 wait states that
+# the compiler's own hazard recognizer inserts after the 8-pass 32x32x16 ops on gfx950
+# (s_nop 11).  MFMA -> MFMA accumulation into the same registers is interlocked by the
+# hardware.  These checks walk the emitted code.
+RESULT_WAIT_STATES = 12
 REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)\b)")
 
 
@@ -200,7 +202,8 @@ def test_mfma_source_hazards(asm):
 
 
 def test_mfma_result_hazards(asm):
-    """No VALU instruction touches an MFMA destination less than 18 wait states after it."""
+    """No VALU instruction touches an MFMA destination less than RESULT_WAIT_STATES wait
+    states after it."""
     problems = []
     for name, seq in instruction_stream(asm).items():
         for i, (ln, _, lab) in enumerate(seq):
@@ -209,7 +212,7 @@ def test_mfma_result_hazards(asm):
             op, args = split_ops(ln)
             dst = regs_of(args[0])
             ws, j = 0, i + 1
-            while j < len(seq) and ws < 18:
+            while j < len(seq) and ws < RESULT_WAIT_STATES:
                 nln, _, nlab = seq[j]
                 if nlab or nln.startswith("s_cbranch") or nln.startswith("s_branch"):
                     break
@@ -231,9 +234,9 @@ def test_hazard_checker_catches_planted_hazards():
     after an MFMA result (planted in a synthetic stream, not in the kernels)."""
     good = ("_Zattn_fwd_kernel_t:\n\tds_read_b128 v[4:7], v1\n\ts_waitcnt lgkmcnt(0)\n"
             "\ts_nop 1\n\tv_mfma_f32_32x32x16_f16 a[0:15], v[4:7], v[8:11], a[0:15]\n"
-            "\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\tv_accvgpr_read_b32 v2, a3\n\ts_endpgm\n")
+            "\ts_nop 11\n\tv_accvgpr_read_b32 v2, a3\n\ts_endpgm\n")
     bad_src = good.replace("\ts_nop 1\n", "\tv_mov_b32_e32 v9, 0\n")
-    bad_dst = good.replace("\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n", "\ts_nop 3\n")
+    bad_dst = good.replace("\ts_nop 11\n", "\ts_nop 10\n")
     test_mfma_source_hazards(good)
     test_mfma_result_hazards(good)
     with pytest.raises(AssertionError):
