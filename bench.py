@@ -43,10 +43,14 @@ def flops_pages(q_len, kv_len, hd, heads_q, batch=1):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with // comments and blank space removed, so that editing
+    a comment does not invalidate counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = re.sub(r"//[^\n]*", "", f.read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

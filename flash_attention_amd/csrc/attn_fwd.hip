@@ -3,9 +3,10 @@
 //
 // Method: the flash-attention forward of the "Xe2 (Lunar Lake/LNL, Battlemage/BMG) ESIMD
 // Flash Attention -- HD=256" page (GQA, online softmax over key tiles, one reciprocal of
-// the row sum at the end: sections "Key Optimization Insights / What Worked") with the fp32-softmax data flow of "Xe2 Sdp Bf16"
-// (section "Kernel Architecture: bf16io", data-flow diagram).  The Xe2 register and SLM
-// choreography is not reused; the layout below is built around CDNA4's 32x32x16 MFMA.
+// the row sum at the end: sections "Key Optimization Insights / What Worked") with the
+// fp32-softmax data flow of "Xe2 Sdp Bf16" (section "Kernel Architecture: bf16io",
+// data-flow diagram).  The Xe2 register and SLM choreography is not reused; the layout
+// below is built around CDNA4's 32x32x16 MFMA.
 //
 // Work decomposition.  A workgroup is 4 wavefronts and owns BLOCK_M = 128*QB query rows of
 // one query head; each wavefront owns 32*QB whole rows, so a row's max and sum never cross
@@ -16,20 +17,20 @@
 // (32 keys x 16 dims) and Q^T as the B operand (16 dims x 32 queries, register resident
 // for the whole key loop).  The 32x32 fp32 result then holds one query per lane column:
 // lane l owns query l%32 and 16 of the 32 keys, the other 16 sitting in lane l^32.  Row
-// max = an in-lane max plus one cross-half exchange; the row sum stays per-lane until the
-// end.  Those same registers, rounded to 16 bits, are directly the B operand of
+// max = an in-lane max plus one cross-half exchange (needed for the first tile only: its
+// maximum is the reference for the whole sweep); the row sum stays per-lane until the end.  Those same registers, rounded to 16 bits, are directly the B operand of
 // O^T += V^T * P^T (k index = key): no trip through LDS for P.  The key order inside the
 // B operand is fixed by the accumulator layout, so V^T must be read in that same
 // key order, which the transposing LDS reads of V provide.  O^T lives in 32x32 accumulators
 // with one query per lane column as well.
 //
 // Pipeline.  K and V tiles of 32 keys are copied straight from HBM into LDS (no register
-// staging) into four stages.  Iteration t of the key loop reads K of tile t (S^T) and V of
-// tile t-1 (the P.V product of the previous tile, under which the softmax of tile t runs);
-// tile t+1 is landing, and tile t+2 is issued at the one workgroup barrier of the
-// iteration.  Each wavefront owns 64 query rows (two 32-row MFMA blocks), so every K and V
-// fragment read from LDS feeds two MFMAs; Q stays in registers and the output accumulator
-// in AGPRs for the whole key loop.
+// staging) into rings of four stages.  Iteration t of the key loop reads K of tile t (S^T)
+// and V of tile t-1 (the P.V product of the previous tile, under which the softmax of tile
+// t runs); tile t+1 is landing, and tile t+2 is copied after the one workgroup barrier of
+// the iteration, one wave per step.  Each wavefront owns 64 query rows (two 32-row MFMA
+// blocks), so every K and V fragment read from LDS feeds two MFMAs; Q stays in registers
+// and the output accumulator in AGPRs for the whole key loop.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -420,8 +421,9 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   };
 
   // Online softmax of tile t, fp32 in base 2, in slices that run underneath the P.V MFMAs
-  // of tile t-1.  Max slices: this tile's row maximum per query block, then the reference
-  // check.  Exp slices: P = exp2(c*s - m) element by element, row sums, rounding to 16 bits.
+  // of tile t-1.  Max slices (first tile only): its row maximum per query block, which sets
+  // the reference.  Exp slices: P = exp2(c*s - m) element by element, rounding to 16 bits,
+  // partial row sums.
   float mt[QB];
   auto mask_tail = [&](f32x16 (&sacc)[QB], int t) {
     // Keys past Lk (last tile only): the score becomes the worst value, so the key drops
