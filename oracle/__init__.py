@@ -7,8 +7,10 @@ package imports nothing from it: the two share no code.
 Two independent implementations live here:
 
 * ``liboracle.so`` (attn_oracle.c): the plain definition -- scores, row
-  softmax, weighted sum of V, natural-log LSE -- in fp64 with OpenMP over
-  query rows.  This is the oracle the GPU path is judged against.
+  softmax, weighted sum of V, natural-log LSE, optionally causal or over a
+  slice of the keys -- in fp64 with OpenMP over query rows, and the merge of
+  partial results by their LSE.  This is the oracle the GPU path is judged
+  against.
 * ``numpy_ref.attention`` (numpy_ref.py): the same definition written with
   NumPy array operations, used only on tiny shapes to cross-check the C code.
 
@@ -40,7 +42,8 @@ class Oracle:
         self.path = path
         self.lib = ctypes.CDLL(path)
         lib = self.lib
-        common = [_I64] * 6 + [ctypes.c_double, _PTR, _I64, _PTR, _PTR, ctypes.c_int]
+        common = [_I64] * 6 + [ctypes.c_double, ctypes.c_int, _I64, _I64, _PTR, _I64, _PTR, _PTR,
+                               ctypes.c_int]
         lib.oracle_attn_rows_f64.argtypes = [_PTR, _PTR, _PTR] + common
         lib.oracle_attn_rows_f64.restype = ctypes.c_int
         lib.oracle_attn_rows_u16.argtypes = [_PTR, _PTR, _PTR, ctypes.c_int] + common
@@ -50,6 +53,8 @@ class Oracle:
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_merge.argtypes = [_PTR, _PTR, _I64, _I64, _I64, _PTR, _PTR]
+        lib.oracle_merge.restype = ctypes.c_int
 
     def max_threads(self):
         return int(self.lib.oracle_max_threads())
@@ -58,7 +63,8 @@ class Oracle:
         fn = self.lib.oracle_bf16_to_double if dtype == BF16 else self.lib.oracle_f16_to_double
         return fn(int(bits))
 
-    def attention(self, q, k, v, scale, rows=None, nthreads=0):
+    def attention(self, q, k, v, scale, rows=None, nthreads=0, causal=False, key_begin=0,
+                  lk_total=None):
         """Attention rows from the plain definition, in fp64.
 
         q, k, v: torch tensors (float16 / bfloat16 / float64, CPU) or numpy
@@ -66,7 +72,12 @@ class Oracle:
         scale: the softmax scale (pass the float32 value the GPU receives).
         rows: optional int64 array of flat row indices (b*Hq + h)*Lq + i;
         None means every row in order.
-        Returns (O [n, D] float64, LSE [n] float64) as numpy arrays.
+        causal: row i sees global key j only if j <= i + lk_total - Lq.
+        key_begin, lk_total: k and v hold keys [key_begin, key_begin + Lk) of a
+        sequence of lk_total keys (default: the whole sequence, lk_total = Lk);
+        the result is then the partial attention over that slice.
+        Returns (O [n, D] float64, LSE [n] float64) as numpy arrays; a row that
+        sees no key has O = 0 and LSE = -inf.
         """
         qa, dtype = _as_array(q)
         ka, kd = _as_array(k)
@@ -89,8 +100,9 @@ class Oracle:
             rows_ptr = rows_arr.ctypes.data
         o = np.empty((n, D), dtype=np.float64)
         lse = np.empty((n,), dtype=np.float64)
-        args = (B, Hq, Hkv, Lq, Lk, D, float(scale), rows_ptr, n, o.ctypes.data,
-                lse.ctypes.data, int(nthreads))
+        lk_total = Lk if lk_total is None else int(lk_total)
+        args = (B, Hq, Hkv, Lq, Lk, D, float(scale), int(bool(causal)), int(key_begin), lk_total,
+                rows_ptr, n, o.ctypes.data, lse.ctypes.data, int(nthreads))
         if dtype == "f64":
             rc = self.lib.oracle_attn_rows_f64(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
                                                *args)
@@ -98,6 +110,27 @@ class Oracle:
             code = F16 if dtype == "f16" else BF16
             rc = self.lib.oracle_attn_rows_u16(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
                                                code, *args)
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (code %d)" % rc)
+        return o, lse
+
+    def merge(self, o_parts, lse_parts):
+        """Merge partial results over disjoint key ranges (fp64).
+
+        o_parts [P, n, D] and lse_parts [P, n] (array-likes, any float type):
+        part g of row r is the attention of row r over key range g alone.
+        Returns (O [n, D], LSE [n]) float64 with LSE = ln sum_g exp(LSE_g) and
+        O = sum_g exp(LSE_g - LSE) O_g.
+        """
+        op = np.ascontiguousarray(np.asarray(o_parts, dtype=np.float64))
+        lp = np.ascontiguousarray(np.asarray(lse_parts, dtype=np.float64))
+        if op.ndim != 3 or lp.shape != op.shape[:2]:
+            raise ValueError("o_parts must be [P,n,D] and lse_parts [P,n]")
+        P, n, D = op.shape
+        o = np.empty((n, D), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        rc = self.lib.oracle_merge(op.ctypes.data, lp.ctypes.data, P, n, D, o.ctypes.data,
+                                   lse.ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected its arguments (code %d)" % rc)
         return o, lse
@@ -137,5 +170,10 @@ def default():
     return _default
 
 
-def attention(q, k, v, scale, rows=None, nthreads=0):
-    return default().attention(q, k, v, scale, rows=rows, nthreads=nthreads)
+def attention(q, k, v, scale, rows=None, nthreads=0, causal=False, key_begin=0, lk_total=None):
+    return default().attention(q, k, v, scale, rows=rows, nthreads=nthreads, causal=causal,
+                               key_begin=key_begin, lk_total=lk_total)
+
+
+def merge(o_parts, lse_parts):
+    return default().merge(o_parts, lse_parts)

@@ -27,6 +27,23 @@
  * included).  Subtracting m in step 2 is exact algebra for stability, not a
  * step of the online softmax.
  *
+ * Causal masking (optional).  Query row i sees key j only if
+ * j <= i + (Lk - Lq): the diagonal is aligned to the end of both sequences, so
+ * the Lq queries are read as the last Lq positions of a sequence whose first
+ * Lk positions are the keys.  The SyclKittens summary (sections B.1.2, E.4,
+ * E.6) names partial-tile causal masking and causal runs with as few as 8
+ * query rows against long key sequences, for which only this alignment gives
+ * every query a key; with Lq = Lk it is the usual lower-triangular mask.  The
+ * pages do not spell the alignment out; this is the reading taken.  A row that
+ * sees no key at all (possible only when Lq > Lk) has an empty sum: its output
+ * is 0 and its LSE is ln 0 = -inf.
+ *
+ * Key ranges (optional).  K and V may hold a slice [key_begin, key_begin + Lk)
+ * of a longer key sequence of length lk_total: the causal test then uses the
+ * slice's global key index, and the result is the attention of each row over
+ * the keys of the slice alone -- the partial result that, merged by LSE with
+ * the partials over the other slices, gives the full one.
+ *
  * Precision: every product and sum is fp64.  16-bit inputs are widened
  * exactly to double first ("Xe2 Sdp Bf16", section "Correctness Testing",
  * "CPU reference must match input type": the reference consumes the same
@@ -75,12 +92,18 @@ static double widen(uint16_t bits, int dtype) {
   return dtype == ORACLE_BF16 ? oracle_bf16_to_double(bits) : oracle_f16_to_double(bits);
 }
 
-/* One query row against one key/value head.  e is caller scratch of Lk. */
-static void attend_row(const double* qrow, const double* K, const double* V, int64_t Lk,
+/* One query row against the first nvis keys of one key/value head (nvis <= Lk
+ * of the slice; nvis = Lk without causal masking).  e is caller scratch. */
+static void attend_row(const double* qrow, const double* K, const double* V, int64_t nvis,
                        int64_t D, double scale, double* orow, double* lse, double* e) {
+  for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+  if (nvis <= 0) { /* no key visible: empty sum */
+    *lse = -INFINITY;
+    return;
+  }
   /* step 1: scores */
   double m = -INFINITY;
-  for (int64_t j = 0; j < Lk; ++j) {
+  for (int64_t j = 0; j < nvis; ++j) {
     const double* kj = K + j * D;
     double dot = 0.0;
     for (int64_t d = 0; d < D; ++d) dot += qrow[d] * kj[d];
@@ -89,13 +112,12 @@ static void attend_row(const double* qrow, const double* K, const double* V, int
   }
   /* step 2: softmax weights (unnormalised) and their sum */
   double sum = 0.0;
-  for (int64_t j = 0; j < Lk; ++j) {
+  for (int64_t j = 0; j < nvis; ++j) {
     e[j] = exp(e[j] - m);
     sum += e[j];
   }
   /* step 3: weighted sum of value rows, normalised */
-  for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
-  for (int64_t j = 0; j < Lk; ++j) {
+  for (int64_t j = 0; j < nvis; ++j) {
     const double p = e[j] / sum;
     const double* vj = V + j * D;
     for (int64_t d = 0; d < D; ++d) orow[d] += p * vj[d];
@@ -104,16 +126,29 @@ static void attend_row(const double* qrow, const double* K, const double* V, int
   *lse = m + log(sum);
 }
 
-static int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D) {
+/* Keys of the slice visible to query row i. */
+static int64_t visible_keys(int64_t i, int64_t Lq, int64_t Lk, int causal, int64_t key_begin,
+                            int64_t lk_total) {
+  if (!causal) return Lk;
+  /* last visible global key index: i + lk_total - Lq */
+  const int64_t n = i + (lk_total - Lq) - key_begin + 1;
+  return n < 0 ? 0 : (n > Lk ? Lk : n);
+}
+
+static int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                       int causal, int64_t key_begin, int64_t lk_total) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return -2;
   if (Hq % Hkv != 0) return -4;
+  if (causal != 0 && causal != 1) return -11;
+  if (key_begin < 0 || lk_total < key_begin + Lk) return -12;
   return 0;
 }
 
 static int run_rows(const double* q /* NULL: use q16 */, const uint16_t* q16, int dtype,
                     const double* K, const double* V, int64_t B, int64_t Hq, int64_t Hkv,
-                    int64_t Lq, int64_t Lk, int64_t D, double scale, const int64_t* rows,
-                    int64_t nrows, double* o_out, double* lse_out, int nthreads) {
+                    int64_t Lq, int64_t Lk, int64_t D, double scale, int causal,
+                    int64_t key_begin, int64_t lk_total, const int64_t* rows, int64_t nrows,
+                    double* o_out, double* lse_out, int nthreads) {
   const int64_t G = Hq / Hkv;
   const int64_t total = B * Hq * Lq;
   int bad = 0;
@@ -149,7 +184,8 @@ static int run_rows(const double* q /* NULL: use q16 */, const uint16_t* q16, in
           for (int64_t d = 0; d < D; ++d) qrow[d] = widen(q16[flat * D + d], dtype);
         }
         const int64_t kv = (b * Hkv + g) * Lk * D;
-        attend_row(qrow, K + kv, V + kv, Lk, D, scale, o_out + r * D, lse_out + r, e);
+        const int64_t nvis = visible_keys(i, Lq, Lk, causal, key_begin, lk_total);
+        attend_row(qrow, K + kv, V + kv, nvis, D, scale, o_out + r * D, lse_out + r, e);
       }
     }
     free(e);
@@ -159,26 +195,30 @@ static int run_rows(const double* q /* NULL: use q16 */, const uint16_t* q16, in
 }
 
 /* fp64 inputs.  rows == NULL selects all B*Hq*Lq rows in order (nrows must
- * then equal that count).  o_out is nrows x D, lse_out is nrows.
+ * then equal that count).  o_out is nrows x D, lse_out is nrows.  causal is
+ * 0 or 1; K and V hold keys [key_begin, key_begin + Lk) of a sequence of
+ * lk_total keys (0 and Lk for the whole sequence).
  * Returns 0, or a negative code for a bad shape / row index / allocation. */
 int oracle_attn_rows_f64(const double* q, const double* k, const double* v, int64_t B,
                          int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                         double scale, const int64_t* rows, int64_t nrows, double* o_out,
-                         double* lse_out, int nthreads) {
-  int rc = check_shape(B, Hq, Hkv, Lq, Lk, D);
+                         double scale, int causal, int64_t key_begin, int64_t lk_total,
+                         const int64_t* rows, int64_t nrows, double* o_out, double* lse_out,
+                         int nthreads) {
+  int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, causal, key_begin, lk_total);
   if (rc) return rc;
   if (!rows && nrows != B * Hq * Lq) return -9;
-  return run_rows(q, NULL, 0, k, v, B, Hq, Hkv, Lq, Lk, D, scale, rows, nrows, o_out, lse_out,
-                  nthreads);
+  return run_rows(q, NULL, 0, k, v, B, Hq, Hkv, Lq, Lk, D, scale, causal, key_begin, lk_total,
+                  rows, nrows, o_out, lse_out, nthreads);
 }
 
 /* 16-bit inputs (raw fp16 or bf16 bit patterns, dtype 0 or 1), widened
  * exactly to double before any arithmetic. */
 int oracle_attn_rows_u16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
                          int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                         double scale, const int64_t* rows, int64_t nrows, double* o_out,
-                         double* lse_out, int nthreads) {
-  int rc = check_shape(B, Hq, Hkv, Lq, Lk, D);
+                         double scale, int causal, int64_t key_begin, int64_t lk_total,
+                         const int64_t* rows, int64_t nrows, double* o_out, double* lse_out,
+                         int nthreads) {
+  int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, causal, key_begin, lk_total);
   if (rc) return rc;
   if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -5;
   if (!rows && nrows != B * Hq * Lq) return -9;
@@ -195,11 +235,50 @@ int oracle_attn_rows_u16(const uint16_t* q, const uint16_t* k, const uint16_t* v
     K[x] = widen(k[x], dtype);
     V[x] = widen(v[x], dtype);
   }
-  rc = run_rows(NULL, q, dtype, K, V, B, Hq, Hkv, Lq, Lk, D, scale, rows, nrows, o_out, lse_out,
-                nthreads);
+  rc = run_rows(NULL, q, dtype, K, V, B, Hq, Hkv, Lq, Lk, D, scale, causal, key_begin, lk_total,
+                rows, nrows, o_out, lse_out, nthreads);
   free(K);
   free(V);
   return rc;
+}
+
+/* Merge of partial results over disjoint key ranges.  o_parts is
+ * [nparts][nrows][D], lse_parts [nparts][nrows]: part g of row r is the
+ * attention of row r over key range g alone, with its log-sum-exp.  Since
+ * exp(LSE_g) is that range's sum of exp(scores) and O_g its weighted average,
+ * the whole row has
+ *
+ *   LSE = ln sum_g exp(LSE_g),   O = sum_g exp(LSE_g - LSE) * O_g,
+ *
+ * the merge of online-softmax state that the SyclKittens summary (section I,
+ * context-parallel ring attention) applies after each key shard.  Parts with
+ * LSE_g = -inf (no visible key) carry no weight; if every part is empty the
+ * row is empty too: O = 0, LSE = -inf.  Computed around the largest LSE_g for
+ * range, in fp64.  Returns 0 or a negative code for a bad size. */
+int oracle_merge(const double* o_parts, const double* lse_parts, int64_t nparts, int64_t nrows,
+                 int64_t D, double* o_out, double* lse_out) {
+  if (nparts <= 0 || nrows < 0 || D <= 0) return -2;
+  for (int64_t r = 0; r < nrows; ++r) {
+    double top = -INFINITY;
+    for (int64_t g = 0; g < nparts; ++g)
+      if (lse_parts[g * nrows + r] > top) top = lse_parts[g * nrows + r];
+    double* orow = o_out + r * D;
+    for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+    if (top == -INFINITY) {
+      lse_out[r] = -INFINITY;
+      continue;
+    }
+    double sum = 0.0;
+    for (int64_t g = 0; g < nparts; ++g) sum += exp(lse_parts[g * nrows + r] - top);
+    const double lse = top + log(sum);
+    for (int64_t g = 0; g < nparts; ++g) {
+      const double w = exp(lse_parts[g * nrows + r] - lse);
+      const double* og = o_parts + (g * nrows + r) * D;
+      for (int64_t d = 0; d < D; ++d) orow[d] += w * og[d];
+    }
+    lse_out[r] = lse;
+  }
+  return 0;
 }
 
 /* Number of threads an OpenMP region of this library would use. */

@@ -11,8 +11,12 @@ heads).
 import numpy as np
 
 
-def attention(q, k, v, scale):
-    """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] float64 arrays -> (O [B,Hq,Lq,D], LSE [B,Hq,Lq])."""
+def attention(q, k, v, scale, causal=False):
+    """q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D] float64 arrays -> (O [B,Hq,Lq,D], LSE [B,Hq,Lq]).
+
+    causal: query i keeps key j only where j - i <= Lk - Lq (a triangular mask
+    aligned to the bottom-right corner of the Lq x Lk score matrix); a row with
+    nothing kept gets O = 0 and LSE = -inf."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -20,9 +24,16 @@ def attention(q, k, v, scale):
     k_rep = np.repeat(k, group, axis=1)
     v_rep = np.repeat(v, group, axis=1)
     scores = scale * np.matmul(q, np.swapaxes(k_rep, -1, -2))  # [B,Hq,Lq,Lk]
-    top = scores.max(axis=-1, keepdims=True)
+    Lq, Lk = scores.shape[-2:]
+    keep = np.ones((Lq, Lk), dtype=bool)
+    if causal:
+        keep = np.tril(keep, k=Lk - Lq)
+    scores = np.where(keep, scores, -np.inf)
+    has = keep.any(axis=-1)[:, None]  # [Lq, 1]
+    top = np.where(has, scores.max(axis=-1, keepdims=True), 0.0)
     w = np.exp(scores - top)
     total = w.sum(axis=-1, keepdims=True)
-    out = np.matmul(w / total, v_rep)
-    lse = (top + np.log(total))[..., 0]
+    out = np.matmul(w / np.where(has, total, 1.0), v_rep)
+    with np.errstate(divide="ignore"):
+        lse = (top + np.log(total))[..., 0]
     return out, lse

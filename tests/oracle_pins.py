@@ -31,8 +31,8 @@ def _f64(shape, rng, scale=1.0):
     return rng.standard_normal(shape) * scale
 
 
-def _run(orc, q, k, v, scale, rows=None):
-    o, lse = orc.attention(q, k, v, scale, rows=rows)
+def _run(orc, q, k, v, scale, rows=None, **kw):
+    o, lse = orc.attention(q, k, v, scale, rows=rows, **kw)
     B, Hq, Lq, D = np.asarray(q).shape if not isinstance(q, torch.Tensor) else q.shape
     if rows is None:
         return o.reshape(B, Hq, Lq, D), lse.reshape(B, Hq, Lq)
@@ -305,6 +305,145 @@ def pin_row_subset(orc):
         raise AssertionError("out-of-range row accepted")
 
 
+# ---- causal masking: query i sees key j only if j <= i + (Lk - Lq) ----
+
+def pin_causal_identical_keys(orc):
+    """All keys equal: row i averages exactly its visible values V_0..V_{i+Lk-Lq}, with
+    LSE = scale q.k + ln(count); rows that see no key (Lq > Lk) give O = 0, LSE = -inf.
+    Covers Lq < Lk, Lq = Lk and Lq > Lk, so a shifted or top-left diagonal shows."""
+    rng = _rng(31)
+    D = 8
+    for Lq, Lk in [(5, 24), (9, 9), (30, 24), (1, 6)]:
+        q = rng.integers(-4, 5, size=(1, 2, Lq, D)).astype(np.float64)
+        kk = rng.integers(-4, 5, size=(D,)).astype(np.float64)
+        k = np.broadcast_to(kk, (1, 1, Lk, D)).copy()
+        v = _f64((1, 1, Lk, D), rng)
+        o, lse = _run(orc, q, k, v, 0.25, causal=True)
+        for h in range(2):
+            for i in range(Lq):
+                n = min(max(i + Lk - Lq + 1, 0), Lk)
+                if n == 0:
+                    assert np.array_equal(o[0, h, i], np.zeros(D)), (Lq, Lk, i)
+                    assert lse[0, h, i] == -np.inf, (Lq, Lk, i)
+                    continue
+                assert np.allclose(o[0, h, i], v[0, 0, :n].mean(axis=0), rtol=1e-13,
+                                   atol=1e-14), (Lq, Lk, i)
+                expect = 0.25 * float(q[0, h, i] @ kk) + math.log(n)
+                assert abs(lse[0, h, i] - expect) <= 1e-13, (Lq, Lk, i)
+
+
+def pin_causal_is_prefix_attention(orc):
+    """A causal row equals the unmasked attention of that row over its visible prefix
+    of keys (bitwise: the same sums in the same order)."""
+    rng = _rng(32)
+    B, Hq, Hkv, Lq, Lk, D = 1, 4, 2, 6, 10, 8
+    q = _f64((B, Hq, Lq, D), rng)
+    k = _f64((B, Hkv, Lk, D), rng)
+    v = _f64((B, Hkv, Lk, D), rng)
+    o, lse = _run(orc, q, k, v, 0.3, causal=True)
+    for i in range(Lq):
+        n = i + Lk - Lq + 1
+        o2, lse2 = _run(orc, q[:, :, i:i + 1], k[:, :, :n], v[:, :, :n], 0.3)
+        assert np.array_equal(o[:, :, i], o2[:, :, 0]) and np.array_equal(lse[:, :, i],
+                                                                           lse2[:, :, 0]), i
+    # and the unmasked result differs wherever a key is hidden
+    o3, _ = _run(orc, q, k, v, 0.3)
+    assert not np.allclose(o3[:, :, 0], o[:, :, 0])
+    assert np.array_equal(o3[:, :, -1], o[:, :, -1])  # the last row sees every key
+
+
+def pin_causal_numpy_crosscheck(orc):
+    """C oracle and NumPy evaluation agree on causal tiny shapes (square, wide, tall)."""
+    rng = _rng(33)
+    for (B, Hq, Hkv, Lq, Lk, D) in [(1, 2, 1, 4, 4, 4), (2, 4, 2, 3, 8, 5), (1, 2, 2, 9, 5, 6),
+                                    (1, 3, 1, 1, 7, 3)]:
+        q = _f64((B, Hq, Lq, D), rng)
+        k = _f64((B, Hkv, Lk, D), rng)
+        v = _f64((B, Hkv, Lk, D), rng)
+        o, lse = _run(orc, q, k, v, 0.45, causal=True)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            o2, lse2 = numpy_ref.attention(q, k, v, 0.45, causal=True)
+        assert np.allclose(o, o2, rtol=1e-13, atol=1e-13), (B, Hq, Hkv, Lq, Lk, D)
+        fin = np.isfinite(lse2)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.allclose(lse[fin], lse2[fin], rtol=1e-13, atol=1e-13)
+
+
+# ---- partial results over key ranges and their merge ----
+
+def pin_key_slice_is_sliced_input(orc):
+    """Without masking, the partial result over keys [a, b) is the attention over the
+    sliced K and V; with causal masking the slice keeps the global key positions."""
+    rng = _rng(34)
+    B, Hq, Hkv, Lq, Lk, D = 1, 2, 1, 5, 12, 4
+    q = _f64((B, Hq, Lq, D), rng)
+    k = _f64((B, Hkv, Lk, D), rng)
+    v = _f64((B, Hkv, Lk, D), rng)
+    a, b = 3, 9
+    o, lse = _run(orc, q, k[:, :, a:b], v[:, :, a:b], 0.6, key_begin=a, lk_total=Lk)
+    o2, lse2 = _run(orc, q, k[:, :, a:b], v[:, :, a:b], 0.6)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    oc, lc = _run(orc, q, k[:, :, a:b], v[:, :, a:b], 0.6, causal=True, key_begin=a,
+                  lk_total=Lk)
+    for i in range(Lq):
+        n = min(max(i + Lk - Lq + 1 - a, 0), b - a)  # visible keys of the slice
+        if n == 0:
+            assert lc[0, 0, i] == -np.inf and not oc[0, 0, i].any()
+            continue
+        oi, li = _run(orc, q[:, :, i:i + 1], k[:, :, a:a + n], v[:, :, a:a + n], 0.6)
+        assert np.array_equal(oc[:, :, i], oi[:, :, 0]) and np.array_equal(lc[:, :, i],
+                                                                           li[:, :, 0])
+
+
+def pin_merge_of_key_splits(orc):
+    """Merging the partial results over a split of the keys gives the full result, with
+    and without causal masking (some causal parts are empty for early rows)."""
+    rng = _rng(35)
+    B, Hq, Hkv, Lq, Lk, D = 1, 2, 1, 7, 20, 6
+    q = _f64((B, Hq, Lq, D), rng, 1.5)
+    k = _f64((B, Hkv, Lk, D), rng, 1.5)
+    v = _f64((B, Hkv, Lk, D), rng)
+    cuts = [0, 4, 13, 17, 20]
+    for causal in (False, True):
+        o, lse = orc.attention(q, k, v, 0.5, causal=causal)
+        parts = [orc.attention(q, k[:, :, a:b], v[:, :, a:b], 0.5, causal=causal, key_begin=a,
+                               lk_total=Lk) for a, b in zip(cuts[:-1], cuts[1:])]
+        om, lm = orc.merge([p[0] for p in parts], [p[1] for p in parts])
+        assert np.allclose(om, o, rtol=1e-13, atol=1e-13), causal
+        assert np.allclose(lm, lse, rtol=1e-13, atol=1e-13), causal
+
+
+def pin_merge_identities(orc):
+    """Merge of one part is that part; empty parts (LSE = -inf) carry no weight; two
+    equal parts give the same output with LSE + ln 2; the order of parts does not
+    matter; two parts with LSE 0 and ln 3 weigh 1/4 and 3/4."""
+    rng = _rng(36)
+    n, D = 5, 4
+    o1 = _f64((n, D), rng)
+    o2 = _f64((n, D), rng)
+    l1 = rng.uniform(-3, 3, n)
+    l2 = rng.uniform(-3, 3, n)
+    om, lm = orc.merge([o1], [l1])
+    assert np.array_equal(om, o1) and np.array_equal(lm, l1)
+    empty = np.full(n, -np.inf)
+    om, lm = orc.merge([o1, np.zeros((n, D))], [l1, empty])
+    assert np.allclose(om, o1, rtol=1e-15, atol=0) and np.allclose(lm, l1, rtol=1e-15, atol=0)
+    om, lm = orc.merge([np.zeros((n, D))] * 2, [empty, empty])
+    assert not om.any() and np.all(lm == -np.inf)
+    om, lm = orc.merge([o1, o1], [l1, l1])
+    assert np.allclose(om, o1, rtol=1e-14, atol=1e-15)
+    assert np.allclose(lm, l1 + math.log(2), rtol=0, atol=1e-14)
+    oa, la = orc.merge([o1, o2], [l1, l2])
+    ob, lb = orc.merge([o2, o1], [l2, l1])
+    assert np.allclose(oa, ob, rtol=1e-14, atol=1e-15) and np.allclose(la, lb, atol=1e-14)
+    om, lm = orc.merge([o1, o2], [np.zeros(n), np.full(n, math.log(3))])
+    assert np.allclose(om, 0.25 * o1 + 0.75 * o2, rtol=1e-14, atol=1e-15)
+    assert np.allclose(lm, math.log(4), rtol=0, atol=1e-14)
+    # large LSE values must not overflow
+    om, lm = orc.merge([o1, o2], [np.full(n, 800.0), np.full(n, 800.0)])
+    assert np.all(np.isfinite(om)) and np.allclose(lm, 800 + math.log(2), atol=1e-12)
+
+
 PINS = [
     pin_worked_example,
     pin_single_key,
@@ -323,4 +462,10 @@ PINS = [
     pin_bf16_widening,
     pin_sixteen_bit_inputs_match_f64,
     pin_row_subset,
+    pin_causal_identical_keys,
+    pin_causal_is_prefix_attention,
+    pin_causal_numpy_crosscheck,
+    pin_key_slice_is_sliced_input,
+    pin_merge_of_key_splits,
+    pin_merge_identities,
 ]

@@ -21,17 +21,37 @@ MUTANTS = {
     "no_max_subtraction": ("e[j] = exp(e[j] - m);", "e[j] = exp(e[j]); m = 0.0;"),
     "lse_log2": ("*lse = m + log(sum);", "*lse = m + log2(sum);"),
     "lse_without_max": ("*lse = m + log(sum);", "*lse = log(sum);"),
-    "transposed_k": ("dot += qrow[d] * kj[d];", "dot += qrow[d] * K[(d * Lk + j) % (Lk * D)];"),
+    "transposed_k": ("dot += qrow[d] * kj[d];", "dot += qrow[d] * K[(d * nvis + j) % (nvis * D)];"),
     "unnormalised_weights": ("const double p = e[j] / sum;", "const double p = e[j];"),
-    "last_key_dropped": ("for (int64_t j = 0; j < Lk; ++j) {\n    const double* kj",
-                         "for (int64_t j = 0; j < Lk - (Lk > 1); ++j) {\n    const double* kj"),
-    "value_row_index": ("const double* vj = V + j * D;", "const double* vj = V + ((j + 1) % Lk) * D;"),
+    "last_key_dropped": ("for (int64_t j = 0; j < nvis; ++j) {\n    const double* kj",
+                         "for (int64_t j = 0; j < nvis - (nvis > 1); ++j) {\n    const double* kj"),
+    "value_row_index": ("const double* vj = V + j * D;",
+                        "const double* vj = V + ((j + 1) % nvis) * D;"),
     "f16_exponent_bias": ("expo - 25", "expo - 24"),
     "f16_subnormal_scale": ("(double)frac, -24", "(double)frac, -25"),
     "bf16_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     "score_sign": ("e[j] = scale * dot;", "e[j] = -scale * dot;"),
     "query_row_offset": ("qrow[d] = widen(q16[flat * D + d], dtype);",
                          "qrow[d] = widen(q16[((flat + 1) % (B * Hq * Lq)) * D + d], dtype);"),
+    # causal masking and key slices
+    "causal_off_by_one": ("const int64_t n = i + (lk_total - Lq) - key_begin + 1;",
+                          "const int64_t n = i + (lk_total - Lq) - key_begin;"),
+    "causal_top_left": ("const int64_t n = i + (lk_total - Lq) - key_begin + 1;",
+                        "const int64_t n = i - key_begin + 1;"),
+    "causal_ignored": ("if (!causal) return Lk;", "return Lk;"),
+    "causal_slice_local": ("const int64_t n = i + (lk_total - Lq) - key_begin + 1;",
+                           "const int64_t n = i + (Lk - Lq) + 1;"),
+    "empty_row_lse_zero": ("    *lse = -INFINITY;\n    return;", "    *lse = 0.0;\n    return;"),
+    # merge
+    "merge_no_max": ("sum += exp(lse_parts[g * nrows + r] - top);",
+                     "sum += exp(lse_parts[g * nrows + r]); top = 0.0;"),
+    "merge_weight_unnormalised": ("const double w = exp(lse_parts[g * nrows + r] - lse);",
+                                  "const double w = exp(lse_parts[g * nrows + r] - top);"),
+    "merge_lse_log2": ("const double lse = top + log(sum);", "const double lse = top + log2(sum);"),
+    "merge_plain_average": ("const double w = exp(lse_parts[g * nrows + r] - lse);",
+                            "const double w = 1.0 / nparts;"),
+    "merge_part_stride": ("const double* og = o_parts + (g * nrows + r) * D;",
+                          "const double* og = o_parts + (r * nparts + g) * D;"),
 }
 
 
