@@ -29,6 +29,8 @@ class Workload:
     dtype: str  # "f16" | "bf16"
     k_mult: float = 1.0
     seed_base: int = 0
+    causal: bool = False  # row i sees key j only if j <= i + Lk - Lq
+    nsplit: int = 1       # key splits of the launch (0: the planner's choice)
 
     @property
     def scale(self):
@@ -36,7 +38,8 @@ class Workload:
 
     @property
     def flops(self):
-        """Attention-forward FLOPs, 4*B*Hq*Lq*Lk*D (the two matrix products)."""
+        """4*B*Hq*Lq*Lk*D: the two matrix products over every (row, key) pair.  Under the
+        causal mask only the visible pairs count; bench.py computes that figure."""
         return 4 * self.B * self.Hq * self.Lq * self.Lk * self.D
 
     @property
@@ -44,9 +47,11 @@ class Workload:
         return torch.float16 if self.dtype == "f16" else torch.bfloat16
 
     def describe(self):
-        return ("B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d %s%s" %
+        return ("B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d %s%s%s%s" %
                 (self.B, self.Hq, self.Hkv, self.Lq, self.Lk, self.D, self.dtype,
-                 " K*%g" % self.k_mult if self.k_mult != 1.0 else ""))
+                 " K*%g" % self.k_mult if self.k_mult != 1.0 else "",
+                 " causal" if self.causal else "",
+                 " nsplit=%d" % self.nsplit if self.nsplit != 1 else ""))
 
 
 # The five workloads of the benchmark plan: the tiny case, the 4K and 8K
@@ -62,6 +67,13 @@ WORKLOADS = {
                                 k_mult=2.0, seed_base=4000),
     "gqa16k_d256": Workload("gqa16k_d256", 1, 32, 2, 16384, 16384, 256, "f16",
                             seed_base=5000),
+    # Next to the plan: the headline shape under the causal mask, and a single sequence of
+    # 1K queries against 16K keys, which leaves half the compute units idle unless the keys
+    # are split (the planner's choice).
+    "gqa16k_d256_causal": Workload("gqa16k_d256_causal", 1, 32, 2, 16384, 16384, 256, "f16",
+                                   seed_base=6000, causal=True),
+    "q1kx16k_d256_split": Workload("q1kx16k_d256_split", 1, 32, 2, 1024, 16384, 256, "f16",
+                                   seed_base=7000, nsplit=0),
 }
 HEADLINE = "gqa16k_d256"
 

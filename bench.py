@@ -37,6 +37,20 @@ def flops_headline(B, Hq, Lq, Lk, D):
     return 4 * B * Hq * Lq * Lk * D
 
 
+def visible_pairs(Lq, Lk, causal):
+    """(query row, key) pairs per head that enter the products: all of them, or under the
+    causal mask (row i sees key j iff j <= i + Lk - Lq) the lower triangle."""
+    if not causal:
+        return Lq * Lk
+    import numpy as np
+    return int(np.clip(np.arange(Lq) + Lk - Lq + 1, 0, Lk).sum())
+
+
+def flops_workload(w):
+    """4*D flops per visible (row, key) pair: 4*B*Hq*Lq*Lk*D without a mask."""
+    return 4 * w.B * w.Hq * visible_pairs(w.Lq, w.Lk, w.causal) * w.D
+
+
 def flops_pages(q_len, kv_len, hd, heads_q, batch=1):
     """The pages' count: both matrix products plus 2 flops per score for the softmax."""
     return batch * (4 * q_len * kv_len * hd * heads_q + 2 * q_len * kv_len * heads_q)
@@ -76,11 +90,15 @@ def compare_rows(o_gpu, lse_gpu, rows, o_ref, lse_ref):
     og = o_gpu.reshape(-1, o_gpu.shape[-1])[idx].double().numpy()
     lg = lse_gpu.reshape(-1)[idx].double().numpy()
     err = og - o_ref
+    # rows that see no key (causal, Lq > Lk) have LSE -inf on both sides
+    empty = np.isneginf(lse_ref)
+    bad_empty = int((lg[empty] != -np.inf).sum() + (og[empty] != 0).sum())
+    lg_f, lr_f = lg[~empty], lse_ref[~empty]
     return {"rows": int(len(rows)),
-            "nonfinite": int((~np.isfinite(og)).sum() + (~np.isfinite(lg)).sum()),
+            "nonfinite": int((~np.isfinite(og)).sum() + (~np.isfinite(lg_f)).sum()) + bad_empty,
             "rel_rms": float(np.sqrt((err ** 2).sum() / (o_ref ** 2).sum())),
             "max_abs": float(np.abs(err).max()),
-            "lse_abs": float(np.abs(lg - lse_ref).max())}
+            "lse_abs": float(np.abs(lg_f - lr_f).max()) if lg_f.size else 0.0}
 
 
 def parse():
@@ -120,16 +138,30 @@ def main():
     scale = float(np.float32(w.scale))
     stream = torch.cuda.current_stream(dev)
     code = fa.dtype_code(q)
-    plan = fa.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code)
-    args_c = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
-              w.Hq, w.Hkv, w.Lq, w.Lk, w.D, scale, code, stream.cuda_stream)
+    flags = fa.ATTN_CAUSAL if w.causal else 0
+    # the planner's launch (kernel name, split choice); the workload may fix the split count
+    plan = fa.attn_plan_ex(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code, flags)
+    nsplit = w.nsplit if w.nsplit else plan.nsplit
+    plan.grid = fa.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code).grid * nsplit
+    # the workspace of a split launch is allocated once, outside the timed region
+    ws_bytes = fa.attn_workspace_bytes(w.B, w.Hq, w.Lq, w.D, nsplit)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if not w.causal and nsplit == 1:
+        args_c = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, scale, code, stream.cuda_stream)
+        launch = fa.attn_fwd_stream
+    else:
+        args_c = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, scale, code, flags, nsplit, ws.data_ptr(),
+                  ws_bytes, stream.cuda_stream)
+        launch = fa.attn_fwd_ex
     torch.cuda.synchronize()
-    print("[bench] %s inputs ready in %.1fs; plan %s grid=%d block_m=%d block_n=%d" %
+    print("[bench] %s inputs ready in %.1fs; plan %s grid=%d block_m=%d block_n=%d nsplit=%d" %
           (w.describe(), time.time() - t0, plan.kernel.decode(), plan.grid, plan.block_m,
-           plan.block_n), file=sys.stderr, flush=True)
+           plan.block_n, nsplit), file=sys.stderr, flush=True)
 
     def step():
-        rc = fa.attn_fwd_stream(*args_c)
+        rc = launch(*args_c)
         if rc != 0:
             raise fa.AttnError(rc, fa.attn_strerror(rc))
 
@@ -152,7 +184,7 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = wall * 1e3 / args.steps
     kern_avg = e0.elapsed_time(e1) / args.steps
-    flops = flops_headline(w.B, w.Hq, w.Lq, w.Lk, w.D)
+    flops = flops_workload(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_avg * 1e-3) / 1e12
     print("[bench] kernel ms (events, mean over %d launches) %.4f; wall/step %.4f ms" %
@@ -183,12 +215,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Lq": w.Lq,
                    "Lk": w.Lk, "D": w.D, "in_dtype": w.dtype, "k_mult": w.k_mult,
-                   "scale": scale, "causal": False, "kernel": plan.kernel.decode(),
-                   "block_m": plan.block_m, "block_n": plan.block_n, "grid": plan.grid},
+                   "scale": scale, "causal": w.causal, "nsplit": nsplit,
+                   "kernel": plan.kernel.decode(), "block_m": plan.block_m,
+                   "block_n": plan.block_n, "grid": plan.grid},
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
         "kernel_ms_mean": round(kern_avg, 4),
-        "tflops_pages_formula": round(flops_pages(w.Lq, w.Lk, w.D, w.Hq, w.B) /
-                                      (ms_per_step * 1e-3) / 1e12, 2),
+        "tflops_pages_formula": (round(flops_pages(w.Lq, w.Lk, w.D, w.Hq, w.B) /
+                                       (ms_per_step * 1e-3) / 1e12, 2)
+                                 if not w.causal else None),
         "roofline": None,
         "cpu_baseline": None,
     }
@@ -204,9 +238,13 @@ def main():
         threads = len(os.sched_getaffinity(0))
         orc = oracle.default()
         c0 = time.perf_counter()
-        o_ref, lse_ref = orc.attention(q, k, v, scale, rows=rows, nthreads=threads)
+        o_ref, lse_ref = orc.attention(q, k, v, scale, rows=rows, nthreads=threads,
+                                       causal=w.causal)
         csec = time.perf_counter() - c0
-        cpu_flops = 4 * w.Lk * w.D * len(rows)
+        i_rows = np.asarray(rows) % w.Lq
+        nvis = (np.clip(i_rows + w.Lk - w.Lq + 1, 0, w.Lk) if w.causal
+                else np.full(len(rows), w.Lk))
+        cpu_flops = 4 * w.D * int(nvis.sum())
         cm = compare_rows(o.cpu(), lse.cpu(), rows, o_ref, lse_ref)
         out["cpu_baseline"] = {
             "value": round(cpu_flops / csec / 1e12, 6), "unit": "TFLOPS", "cores": threads,
@@ -214,7 +252,7 @@ def main():
             "sample": "%d query rows of this workload (seeded: %d random + first/last tiles "
                       "and end rows of every head), fp64, %.1f s; extrapolated full oracle "
                       "%.0f s" % (len(rows), min(args.cpu_rows, w.B * w.Hq * w.Lq), csec,
-                                  csec * w.B * w.Hq * w.Lq / len(rows))}
+                                  csec * flops / cpu_flops)}
         out["parity_on_sample"] = cm
     print(json.dumps(out), flush=True)
     return 0

@@ -55,11 +55,20 @@ struct Params {
   const uint16_t* __restrict__ q;
   const uint16_t* __restrict__ k;
   const uint16_t* __restrict__ v;
-  uint16_t* __restrict__ o;
+  uint16_t* __restrict__ o;  // final output (o_part == nullptr)
   float* __restrict__ lse;
+  // Partial results over key splits (nullptr: one split, final output in o): split s of
+  // row r at o_part[(s * part_rows + r) * D], its LSE at lse_part[s * part_rows + r].
+  float* __restrict__ o_part;
+  float* __restrict__ lse_part;
+  int64_t part_rows;  // B * Hq * Lq
   int Hq, Hkv, G, Lq, Lk;
   int n_qtiles;
-  float c;  // scale * log2(e): scores are kept in base-2 units
+  int nsplit;     // key splits (workgroups per query tile)
+  int split_len;  // keys per split, a multiple of the key tile (split s: [s*len, (s+1)*len))
+  int diag;       // row i sees key j only if j <= i + diag (Lk - Lq if causal, else Lk)
+  int causal;     // heaviest query tiles first (their key range is the longest)
+  float c;        // scale * log2(e): scores are kept in base-2 units
 };
 
 // 32x32x16 MFMA issued through inline asm.  The score accumulator is pinned to VGPRs ("v":
@@ -232,26 +241,44 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Workgroups are dealt round-robin to the 8 XCDs; renumber so each XCD runs a contiguous
-  // range of (batch, head, query tile) and its concurrent workgroups share key/value heads
-  // in that XCD's L2.
+  // range of (batch, head, query tile, key split) and its concurrent workgroups share
+  // key/value heads in that XCD's L2.
   const int nblk = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
   // (integer division is expanded into VALU code; readfirstlane keeps the results in SGPRs)
-  const int qtile = __builtin_amdgcn_readfirstlane(logical % p.n_qtiles);
-  const int bh = __builtin_amdgcn_readfirstlane(logical / p.n_qtiles);  // b*Hq + hq
+  const int split = __builtin_amdgcn_readfirstlane(logical % p.nsplit);
+  const int tile_id = __builtin_amdgcn_readfirstlane(logical / p.nsplit);
+  int qtile = __builtin_amdgcn_readfirstlane(tile_id % p.n_qtiles);
+  // causal: the last query tiles see the most keys; dispatching them first keeps the
+  // light tiles for the end of the grid
+  if (p.causal) qtile = p.n_qtiles - 1 - qtile;
+  const int bh = __builtin_amdgcn_readfirstlane(tile_id / p.n_qtiles);  // b*Hq + hq
   const int hq = __builtin_amdgcn_readfirstlane(bh % p.Hq);
   const int b = __builtin_amdgcn_readfirstlane(bh / p.Hq);
   const int hkv = __builtin_amdgcn_readfirstlane(hq / p.G);
 
-  const uint16_t* qh = p.q + (size_t)bh * p.Lq * D;
-  const uint16_t* kh = p.k + ((size_t)b * p.Hkv + hkv) * p.Lk * D;
-  const uint16_t* vh = p.v + ((size_t)b * p.Hkv + hkv) * p.Lk * D;
-  const int qrow0 = qtile * BM + wave * 32 * QB;
+  // Keys of this workgroup: its split [kbeg, kbeg + split_len), cut at Lk and, under the
+  // causal mask, after the last key its last query row sees.  Tile t holds keys
+  // kbeg + 32t .. kbeg + 32t + 31.
   const int Lk = p.Lk;
-  const int ntiles = (Lk + BN - 1) / BN;
-  const int nfull = Lk / BN;  // tiles whose 32 keys are all valid; tile nfull is partial
+  const int kbeg = min(split * p.split_len, Lk);
+  const int qlast = min(qtile * BM + BM - 1, p.Lq - 1);
+  const int kend = min(min(Lk, kbeg + p.split_len), qlast + p.diag + 1);
+  const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
+  const int nfull = (Lk - kbeg) / BN;  // tiles whose 32 rows all exist in K and V
+
+  const uint16_t* qh = p.q + (size_t)bh * p.Lq * D;
+  const uint16_t* kh = p.k + (((size_t)b * p.Hkv + hkv) * p.Lk + kbeg) * D;
+  const uint16_t* vh = p.v + (((size_t)b * p.Hkv + hkv) * p.Lk + kbeg) * D;
+  const int qrow0 = qtile * BM + wave * 32 * QB;
+  // Key limits relative to kbeg: keys past key_lim do not exist, and row r sees keys up
+  // to r + row_off.  Every row of this wave sees keys 0..wave_lim; tiles past that need
+  // masks.
+  const int key_lim = Lk - 1 - kbeg;
+  const int row_off = p.diag - kbeg;
+  const int wave_lim = min(key_lim, qrow0 + row_off);
 
   // ---- direct HBM->LDS copies of K and V tiles ----
   // Copy round i of this thread moves tile row r = i*ROWS_PER_LOAD + r0, 16-byte chunk c0
@@ -268,7 +295,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       vk[par] = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_k(par * ROWS_PER_LOAD + r0)) * 16);
     vv = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
   }
-  const uint32_t kv_bytes = static_cast<uint32_t>(Lk) * D * 2;
+  const uint32_t kv_bytes = static_cast<uint32_t>(Lk - kbeg) * D * 2;
   // K and V base addresses of this head as wave-uniform 64-bit values (scalar registers),
   // so that the per-tile descriptors are scalar arithmetic.
   auto uniform64 = [](const void* ptr) {
@@ -335,7 +362,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = src[2 * kk];
   }
 
-  issue_tile(0, 0);
+  if (ntiles > 0) issue_tile(0, 0);
   if (ntiles > 1) issue_tile(1, 1);
   if (tid == 0) restart_flag[0] = 0;
 
@@ -425,21 +452,27 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // the reference.  Exp slices: P = exp2(c*s - m) element by element, rounding to 16 bits,
   // partial row sums.
   float mt[QB];
-  auto mask_tail = [&](f32x16 (&sacc)[QB], int t) {
-    // Keys past Lk (last tile only): the score becomes the worst value, so the key drops
-    // out of the maximum and its weight exp2(c*score - m) is exactly 0.  Accumulator
-    // register r of this lane holds key t*BN + 8*(r/4) + 4*hi + r%4.
-    if (t == nfull) {
+  auto mask_keys = [&](f32x16 (&sacc)[QB], int t) {
+    // Keys past Lk, and under the causal mask keys past a row's diagonal: the score becomes
+    // the worst value, so the key drops out of the maximum and its weight
+    // exp2(c*score - m) is exactly 0.  Accumulator register r of this lane holds key
+    // kbeg + t*BN + 8*(r/4) + 4*hi + r%4 of query row qrow0 + 32*qb + l%32.  Only tiles
+    // past the wave's common limit get here (the last tile, the diagonal band).
+    if (t * BN + BN - 1 > wave_lim) {
       // (t laundered: the per-register compares must not be hoisted out of the loop as
-      // 16 loop-invariant lane masks held in scalar registers)
+      // 16 loop-invariant lane masks held in scalar registers; the lane index recomputed
+      // here rather than kept live across the loop)
       int tt = t;
       asm volatile("" : "+s"(tt));
-      const int kvalid = Lk - tt * BN - 4 * hi;
+      const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = qrow0 + qb * 32 + (ln & 31);
+        const int lim = min(key_lim, row + row_off) - tt * BN - 4 * (ln >> 5);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + (r & 3) >= kvalid) sacc[qb][r] = kWorst;
+          if (8 * (r >> 2) + (r & 3) > lim) sacc[qb][r] = kWorst;
+      }
     }
   };
   // Largest scaled score: max (min for a negative scale) as a tree of depth 3 over the 16
@@ -474,6 +507,13 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   auto set_reference = [&]() {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m[qb] = fmaxf(m[qb], mt[qb]);
+  };
+  // A row that sees no key of this split (causal mask) has m = -inf; any finite reference
+  // then gives it weights exp2(-inf) = 0, an empty sum and LSE -inf.  (A row that sees any
+  // key of the split sees its first key, so its first tile has a finite maximum.)
+  auto finite_reference = [&]() {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m[qb] = m[qb] == -__builtin_inff() ? 0.f : m[qb];
   };
   float ev[QB][16], lt[QB];
   auto exp_slice = [&](f32x16 (&sacc)[QB], u32x4 (&pcur)[QB][2], int e0, int e1) {
@@ -541,12 +581,15 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       }
       if (s == 0) {
         mfma_fence_v(sacc[0], sacc[1]);
-        mask_tail(sacc, t);
+        mask_keys(sacc, t);
         if (!PV) row_max(sacc, 0);  // tile 0 only: it fixes the reference
       } else if (s == 1) {
         if (!PV) row_max(sacc, 1);
       } else if (s == 2) {
-        if (!PV) set_reference();
+        if (!PV) {
+          set_reference();
+          finite_reference();
+        }
       } else {
         // the 32 exponentials spread over steps 3..NSTEP-1
         exp_slice(sacc, pcur, 32 * (s - 3) / (NSTEP - 3), 32 * (s - 2) / (NSTEP - 3));
@@ -603,11 +646,12 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       f32x16 sacc[QB];
       qk(kstage(t % NSTAGE), sacc, kf, [] {});
       mfma_fence_v(sacc[0], sacc[1]);
-      mask_tail(sacc, t);
+      mask_keys(sacc, t);
       row_max(sacc, 0);
       row_max(sacc, 1);
       set_reference();
     }
+    finite_reference();
     WAIT_VMCNT(0);
     __syncthreads();  // nobody reads a stage any more
   };
@@ -622,7 +666,9 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // four: the stage of each iteration is a compile-time constant and the two P buffers
   // swap roles without copies.
   u32x4 pa[QB][2], pb2[QB][2];
-  for (;;) {
+  // (a workgroup with no key to look at, under the causal mask or past the last split,
+  // skips the loop: its rows are empty)
+  if (ntiles > 0) for (;;) {
     if (ntiles > 1) WAIT_VMCNT(2 * LOADS);  // tile 0 landed (tile 1 may be in flight)
     else WAIT_VMCNT(0);
     __syncthreads();
@@ -672,16 +718,22 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     }
   }
 
-  // Epilogue: O = O^T / l (one reciprocal per row), LSE = ln2 * (m + log2 l).
+  // Epilogue: O = O^T / l (one reciprocal per row), LSE = ln2 * (m + log2 l).  An empty
+  // row (l = 0) gets O = 0 and LSE = -inf.  Partial results (key splits) are stored in
+  // fp32 for the merge.
   attn_agpr::fence();
   // (lane index recomputed here rather than kept live across the key loop)
   const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const bool partial = p.o_part != nullptr;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l[qb] + __shfl_xor(l[qb], 32);
-    const float inv = 1.0f / lt;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int row = qrow0 + qb * 32 + (lane_e & 31);
-    uint16_t* dst = p.o + ((size_t)bh * p.Lq + min(row, p.Lq - 1)) * D + 4 * (lane_e >> 5);
+    const size_t orow = (size_t)bh * p.Lq + min(row, p.Lq - 1);
+    const size_t prow = (size_t)split * p.part_rows + orow;
+    uint16_t* dst = p.o + orow * D + 4 * (lane_e >> 5);
+    float* pdst = p.o_part + prow * D + 4 * (lane_e >> 5);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       float x[16];
@@ -690,16 +742,27 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       attn_agpr::read4<2>(qb * DB + db, x[8], x[9], x[10], x[11]);
       attn_agpr::read4<3>(qb * DB + db, x[12], x[13], x[14], x[15]);
       if (row < p.Lq) {
+        if (partial) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 w = {Elt<T>::pack2(x[4 * g] * inv, x[4 * g + 1] * inv),
-                           Elt<T>::pack2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * g) = w;
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(pdst + db * 32 + 8 * g) =
+                make_float4(x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv,
+                            x[4 * g + 3] * inv);
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x2 w = {Elt<T>::pack2(x[4 * g] * inv, x[4 * g + 1] * inv),
+                             Elt<T>::pack2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * g) = w;
+          }
         }
       }
     }
-    if (p.lse && lane_e < 32 && row < p.Lq)
-      p.lse[(size_t)bh * p.Lq + row] = (m[qb] + __builtin_log2f(lt)) * 0.69314718055994531f;
+    const float lse_row = (m[qb] + __builtin_log2f(lt)) * 0.69314718055994531f;
+    if (lane_e < 32 && row < p.Lq) {
+      if (partial) p.lse_part[prow] = lse_row;
+      else if (p.lse) p.lse[orow] = lse_row;
+    }
   }
 }
 
@@ -723,6 +786,50 @@ int launch(const Params& prm, int64_t grid, hipStream_t stream) {
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+// Fill the kernel parameters shared by every entry point; the arguments are validated.
+Params make_params(const void* q, const void* k, const void* v, void* o, float* lse,
+                   float* o_part, float* lse_part, int64_t B, int64_t Hq, int64_t Hkv,
+                   int64_t Lq, int64_t Lk, int64_t D, float scale, uint32_t flags,
+                   int64_t nsplit, int block_m) {
+  Params prm;
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.k = static_cast<const uint16_t*>(k);
+  prm.v = static_cast<const uint16_t*>(v);
+  prm.o = static_cast<uint16_t*>(o);
+  prm.lse = lse;
+  prm.o_part = o_part;
+  prm.lse_part = lse_part;
+  prm.part_rows = B * Hq * Lq;
+  prm.Hq = static_cast<int>(Hq);
+  prm.Hkv = static_cast<int>(Hkv);
+  prm.G = static_cast<int>(Hq / Hkv);
+  prm.Lq = static_cast<int>(Lq);
+  prm.Lk = static_cast<int>(Lk);
+  prm.n_qtiles = static_cast<int>((Lq + block_m - 1) / block_m);
+  prm.nsplit = static_cast<int>(nsplit);
+  int64_t b0 = 0, e0 = Lk;
+  attn_split_range(Lk, nsplit, 0, &b0, &e0);
+  prm.split_len = static_cast<int>(e0 - b0);
+  const bool causal = (flags & ATTN_CAUSAL) != 0;
+  prm.diag = static_cast<int>(causal ? Lk - Lq : Lk);
+  prm.causal = causal ? 1 : 0;
+  prm.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  // scale == 0: every weight is 1.  A positive c this small gives c*score below 2^-60 for
+  // any finite fp16/bf16 dot product, so exp2 rounds to exactly 1 and the LSE term c*m
+  // vanishes against ln(Lk) -- the same fp32 results, while masked keys (score -inf) still
+  // get weight exp2(-inf) = 0 instead of exp2(0 * -inf) = NaN.
+  if (prm.c == 0.f) prm.c = 1e-30f;
+  return prm;
+}
+
+int launch_attn(const Params& prm, int64_t D, int in_dtype, int64_t grid, hipStream_t s) {
+  if (D == 128)
+    return in_dtype == ATTN_F16 ? launch<128, _Float16>(prm, grid, s)
+                                : launch<128, __bf16>(prm, grid, s);
+  return in_dtype == ATTN_F16 ? launch<256, _Float16>(prm, grid, s)
+                              : launch<256, __bf16>(prm, grid, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -734,36 +841,73 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   if (rc != ATTN_OK) return rc;
   attn_plan_t plan;
   attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
-  Params prm;
-  prm.q = static_cast<const uint16_t*>(q);
-  prm.k = static_cast<const uint16_t*>(k);
-  prm.v = static_cast<const uint16_t*>(v);
-  prm.o = static_cast<uint16_t*>(o);
-  prm.lse = lse;
-  prm.Hq = static_cast<int>(Hq);
-  prm.Hkv = static_cast<int>(Hkv);
-  prm.G = static_cast<int>(Hq / Hkv);
-  prm.Lq = static_cast<int>(Lq);
-  prm.Lk = static_cast<int>(Lk);
-  prm.n_qtiles = static_cast<int>((Lq + plan.block_m - 1) / plan.block_m);
-  prm.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
-  // scale == 0: every weight is 1.  A positive c this small gives c*score below 2^-60 for
-  // any finite fp16/bf16 dot product, so exp2 rounds to exactly 1 and the LSE term c*m
-  // vanishes against ln(Lk) -- the same fp32 results, while masked keys (score -inf) still
-  // get weight exp2(-inf) = 0 instead of exp2(0 * -inf) = NaN.
-  if (prm.c == 0.f) prm.c = 1e-30f;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (D == 128)
-    return in_dtype == ATTN_F16 ? launch<128, _Float16>(prm, plan.grid, s)
-                                : launch<128, __bf16>(prm, plan.grid, s);
-  return in_dtype == ATTN_F16 ? launch<256, _Float16>(prm, plan.grid, s)
-                              : launch<256, __bf16>(prm, plan.grid, s);
+  const Params prm = make_params(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D,
+                                 scale, 0, 1, plan.block_m);
+  return launch_attn(prm, D, in_dtype, plan.grid, static_cast<hipStream_t>(stream));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
              int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, float scale,
              int in_dtype) {
   return attn_fwd_stream(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, nullptr);
+}
+
+int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
+                     float* lse_part, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
+                     int64_t Lk, int64_t D, float scale, int in_dtype, uint32_t flags,
+                     int64_t nsplit, void* stream) {
+  const int rc = attn_validate_partial(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, D, scale,
+                                       in_dtype, flags, nsplit);
+  if (rc != ATTN_OK) return rc;
+  attn_plan_t plan;
+  attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
+  const Params prm = make_params(q, k, v, nullptr, nullptr, o_part, lse_part, B, Hq, Hkv, Lq,
+                                 Lk, D, scale, flags, nsplit, plan.block_m);
+  return launch_attn(prm, D, in_dtype, plan.grid * nsplit, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, float scale,
+                int in_dtype, uint32_t flags, int64_t nsplit, void* workspace,
+                int64_t workspace_bytes, void* stream) {
+  int rc = attn_validate_ex(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, flags,
+                            nsplit);
+  if (rc != ATTN_OK) return rc;
+  attn_plan_t plan;
+  if (nsplit == 0) {
+    attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, &plan);
+    nsplit = plan.nsplit;
+  } else {
+    attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nsplit == 1) {
+    const Params prm = make_params(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D,
+                                   scale, flags, 1, plan.block_m);
+    return launch_attn(prm, D, in_dtype, plan.grid, s);
+  }
+  // Split keys: partial results into the workspace, then the merge.
+  const int64_t need = attn_workspace_bytes(B, Hq, Lq, D, nsplit);
+  const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
+  if (!workspace || workspace_bytes < need || (ws & 255u) != 0) return ATTN_E_WORKSPACE;
+  const int64_t rows = B * Hq * Lq;
+  const uint64_t wsz = static_cast<uint64_t>(need);
+  auto hits = [&](const void* p, uint64_t n) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return p && a < ws + wsz && ws < a + n;
+  };
+  if (hits(q, uint64_t(rows) * D * 2) || hits(k, uint64_t(B) * Hkv * Lk * D * 2) ||
+      hits(v, uint64_t(B) * Hkv * Lk * D * 2) || hits(o, uint64_t(rows) * D * 2) ||
+      hits(lse, uint64_t(rows) * 4))
+    return ATTN_E_WORKSPACE;
+  float* o_part = static_cast<float*>(workspace);
+  const int64_t obytes = (nsplit * rows * D * 4 + 255) / 256 * 256;
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + obytes);
+  const Params prm = make_params(q, k, v, nullptr, nullptr, o_part, lse_part, B, Hq, Hkv, Lq,
+                                 Lk, D, scale, flags, nsplit, plan.block_m);
+  rc = launch_attn(prm, D, in_dtype, plan.grid * nsplit, s);
+  if (rc != ATTN_OK) return rc;
+  return attn_merge(o_part, lse_part, nsplit, rows, D, o, lse, in_dtype, stream);
 }
 
 }  // extern "C"

@@ -5,6 +5,7 @@
 // Validation rejects rather than mis-computes: an unsupported head dimension is an error,
 // the way the generalised ESIMD GEMM of the GEMM guide "XPU 算子开发最佳实践：GEMM 高性能优化指南"
 // (section 四, ESIMD) checks its shape on the host before dispatching to a compiled template.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -42,7 +43,7 @@ bool plan_for_d(int64_t D, PlanInternal* p) {
 }
 
 int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                int in_dtype) {
+                int in_dtype, int64_t nsplit = 1) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return ATTN_E_SHAPE;
   if (D != 128 && D != 256) return ATTN_E_HEADDIM;
   if (Hq % Hkv != 0) return ATTN_E_GQA;
@@ -54,6 +55,79 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int6
   plan_for_d(D, &p);
   const int64_t qtiles = (Lq + p.block_m - 1) / p.block_m;
   if (qtiles > lim / Hq || qtiles * Hq > lim / B) return ATTN_E_SHAPE;  // grid < 2^31
+  if (qtiles * Hq * B > lim / nsplit) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+constexpr int64_t kSplitAlign = 64;  // keys per split: a multiple of two key tiles
+
+int64_t split_len_of(int64_t Lk, int64_t nsplit) {
+  const int64_t per = (Lk + nsplit - 1) / nsplit;
+  return (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Cost model of the planner, in units of one key tile (32 keys) of one workgroup.  The GPU
+// runs one workgroup per compute unit (256 of them); a workgroup costs its key tiles plus
+// a fixed overhead for pipeline fill, drain and epilogue; splitting adds the partial
+// results' round trip through HBM and a second launch.
+double split_cost(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int64_t D, int64_t ns,
+                  int block_m) {
+  constexpr double kCUs = 256, kOverheadTiles = 4, kLaunchTiles = 3;
+  const int64_t len = split_len_of(Lk, ns);
+  const int64_t used = (Lk + len - 1) / len;  // splits with keys
+  const int64_t wg = (Lq + block_m - 1) / block_m * Hq * B * used;
+  const double rounds = std::ceil(static_cast<double>(wg) / kCUs);
+  double cost = rounds * (static_cast<double>(len) / 32.0 + kOverheadTiles);
+  if (ns > 1) {
+    // One tile of one workgroup: block_m x 32 x D x 4 flop at ~1/256 of ~1.2 PFLOP/s; the
+    // partials are written and read in fp32 and the output written once, at ~4 TB/s.
+    const double tile_s = static_cast<double>(block_m) * 32.0 * D * 4.0 / (1.2e15 / kCUs);
+    const double bytes = static_cast<double>(B * Hq * Lq) * D * (8.0 * used + 2.0);
+    cost += bytes / 4e12 / tile_s + kLaunchTiles;
+  }
+  return cost;
+}
+
+int64_t choose_nsplit(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int64_t D,
+                      int block_m) {
+  int64_t best = 1;
+  double best_cost = split_cost(B, Hq, Lq, Lk, D, 1, block_m);
+  for (int64_t ns = 2; ns <= 32; ++ns) {
+    if (split_len_of(Lk, ns) < 512) break;  // splits shorter than 16 tiles do not pay
+    const double c = split_cost(B, Hq, Lq, Lk, D, ns, block_m);
+    if (c < 0.95 * best_cost) {  // a split must win clearly
+      best = ns;
+      best_cost = c;
+    }
+  }
+  return best;
+}
+
+const char* kernel_name(int64_t D, int in_dtype, uint32_t flags) {
+  const bool c = (flags & ATTN_CAUSAL) != 0;
+  if (D == 128)
+    return in_dtype == ATTN_F16 ? (c ? "attn_fwd_d128_f16_causal" : "attn_fwd_d128_f16")
+                                : (c ? "attn_fwd_d128_bf16_causal" : "attn_fwd_d128_bf16");
+  return in_dtype == ATTN_F16 ? (c ? "attn_fwd_d256_f16_causal" : "attn_fwd_d256_f16")
+                              : (c ? "attn_fwd_d256_bf16_causal" : "attn_fwd_d256_bf16");
+}
+
+int fill_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int64_t D, int in_dtype,
+              uint32_t flags, int64_t nsplit, attn_plan_t* plan) {
+  PlanInternal p;
+  plan_for_d(D, &p);
+  plan->block_m = p.block_m;
+  plan->block_n = p.bn;
+  plan->waves = attn_cfg::kWaves;
+  plan->lds_bytes = p.lds;
+  plan->grid = ((Lq + p.block_m - 1) / p.block_m) * Hq * B * nsplit;
+  std::memset(plan->kernel, 0, sizeof plan->kernel);
+  std::strncpy(plan->kernel, kernel_name(D, in_dtype, flags), sizeof plan->kernel - 1);
+  plan->nsplit = static_cast<int32_t>(nsplit);
+  plan->split_len = static_cast<int32_t>(nsplit == 1 ? Lk : split_len_of(Lk, nsplit));
+  plan->workspace_bytes = attn_workspace_bytes(B, Hq, Lq, D, nsplit);
   return ATTN_OK;
 }
 
@@ -83,23 +157,114 @@ int attn_validate(const void* q, const void* k, const void* v, const void* o, co
   return ATTN_OK;
 }
 
+int attn_validate_ex(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                     int64_t D, float scale, int in_dtype, uint32_t flags, int64_t nsplit) {
+  if (flags & ~ATTN_CAUSAL) return ATTN_E_FLAGS;
+  if (nsplit < 0 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
+  const int rc = attn_validate(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype);
+  if (rc != ATTN_OK) return rc;
+  return check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, nsplit > 0 ? nsplit : ATTN_MAX_SPLITS);
+}
+
+int attn_validate_partial(const void* q, const void* k, const void* v, const float* o_part,
+                          const float* lse_part, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
+                          int64_t Lk, int64_t D, float scale, int in_dtype, uint32_t flags,
+                          int64_t nsplit) {
+  if (!q || !k || !v || !o_part || !lse_part) return ATTN_E_NULLPTR;
+  if (flags & ~ATTN_CAUSAL) return ATTN_E_FLAGS;
+  if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
+  int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, nsplit);
+  if (rc != ATTN_OK) return rc;
+  if (!std::isfinite(scale)) return ATTN_E_SCALE;
+  auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (mis16(q) || mis16(k) || mis16(v) || mis16(o_part)) return ATTN_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0) return ATTN_E_ALIGN;
+  const uint64_t qbytes = uint64_t(B) * Hq * Lq * D * 2;
+  const uint64_t kvbytes = uint64_t(B) * Hkv * Lk * D * 2;
+  const uint64_t pbytes = uint64_t(nsplit) * B * Hq * Lq * D * 4;
+  const uint64_t lbytes = uint64_t(nsplit) * B * Hq * Lq * 4;
+  const void* outs[2] = {o_part, lse_part};
+  const uint64_t osz[2] = {pbytes, lbytes};
+  for (int i = 0; i < 2; ++i)
+    if (overlaps(outs[i], osz[i], q, qbytes) || overlaps(outs[i], osz[i], k, kvbytes) ||
+        overlaps(outs[i], osz[i], v, kvbytes))
+      return ATTN_E_ALIAS;
+  if (overlaps(o_part, pbytes, lse_part, lbytes)) return ATTN_E_ALIAS;
+  return ATTN_OK;
+}
+
+int attn_validate_merge(const float* o_part, const float* lse_part, int64_t nsplit,
+                        int64_t rows, int64_t D, const void* o, const float* lse,
+                        int out_dtype) {
+  if (!o_part || !lse_part || !o) return ATTN_E_NULLPTR;
+  if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
+  if (rows <= 0 || D <= 0) return ATTN_E_SHAPE;
+  if (D % 8 != 0 || D > 4096) return ATTN_E_HEADDIM;
+  if (out_dtype != ATTN_F16 && out_dtype != ATTN_BF16 && out_dtype != ATTN_F32)
+    return ATTN_E_DTYPE;
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  // part offsets (s * rows + row) * D stay below 2^62; blocks of 256 threads below 2^31
+  if (rows > (int64_t(1) << 40) / D / nsplit) return ATTN_E_SHAPE;
+  if ((rows * (D / 8) + 255) / 256 > lim) return ATTN_E_SHAPE;
+  auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (mis16(o_part) || mis16(o)) return ATTN_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0) return ATTN_E_ALIGN;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_E_ALIGN;
+  const uint64_t esz = out_dtype == ATTN_F32 ? 4 : 2;
+  const uint64_t pbytes = uint64_t(nsplit) * rows * D * 4, lpbytes = uint64_t(nsplit) * rows * 4;
+  const uint64_t obytes = uint64_t(rows) * D * esz, lbytes = uint64_t(rows) * 4;
+  if (overlaps(o, obytes, o_part, pbytes) || overlaps(o, obytes, lse_part, lpbytes))
+    return ATTN_E_ALIAS;
+  if (lse && (overlaps(lse, lbytes, o_part, pbytes) || overlaps(lse, lbytes, lse_part, lpbytes) ||
+              overlaps(lse, lbytes, o, obytes)))
+    return ATTN_E_ALIAS;
+  return ATTN_OK;
+}
+
+int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int64_t* end) {
+  if (!begin || !end) return ATTN_E_NULLPTR;
+  if (Lk <= 0) return ATTN_E_SHAPE;
+  if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS || s < 0 || s >= nsplit) return ATTN_E_SPLIT;
+  if (nsplit == 1) {
+    *begin = 0;
+    *end = Lk;
+    return ATTN_OK;
+  }
+  const int64_t len = split_len_of(Lk, nsplit);
+  *begin = std::min(s * len, Lk);
+  *end = std::min(*begin + len, Lk);
+  return ATTN_OK;
+}
+
+int64_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t nsplit) {
+  if (B <= 0 || Hq <= 0 || Lq <= 0 || D <= 0) return ATTN_E_SHAPE;
+  if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
+  if (nsplit == 1) return 0;
+  const int64_t rows = B * Hq * Lq;
+  if (rows > (int64_t(1) << 40) / D / nsplit) return ATTN_E_SHAPE;
+  return align256(nsplit * rows * D * 4) + align256(nsplit * rows * 4);
+}
+
 int attn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
               int in_dtype, attn_plan_t* plan) {
   if (!plan) return ATTN_E_NULLPTR;
   int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype);
   if (rc != ATTN_OK) return rc;
+  return fill_plan(B, Hq, Lq, Lk, D, in_dtype, 0, 1, plan);
+}
+
+int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                 int in_dtype, uint32_t flags, attn_plan_t* plan) {
+  if (!plan) return ATTN_E_NULLPTR;
+  if (flags & ~ATTN_CAUSAL) return ATTN_E_FLAGS;
+  int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype);
+  if (rc != ATTN_OK) return rc;
   PlanInternal p;
   plan_for_d(D, &p);
-  plan->block_m = p.block_m;
-  plan->block_n = p.bn;
-  plan->waves = attn_cfg::kWaves;
-  plan->lds_bytes = p.lds;
-  plan->grid = ((Lq + p.block_m - 1) / p.block_m) * Hq * B;
-  std::memset(plan->kernel, 0, sizeof plan->kernel);
-  const char* name = D == 128 ? (in_dtype == ATTN_F16 ? "attn_fwd_d128_f16" : "attn_fwd_d128_bf16")
-                              : (in_dtype == ATTN_F16 ? "attn_fwd_d256_f16" : "attn_fwd_d256_bf16");
-  std::strncpy(plan->kernel, name, sizeof plan->kernel - 1);
-  return ATTN_OK;
+  int64_t ns = choose_nsplit(B, Hq, Lq, Lk, D, p.block_m);
+  while (ns > 1 && check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, ns) != ATTN_OK) --ns;
+  return fill_plan(B, Hq, Lq, Lk, D, in_dtype, flags, ns, plan);
 }
 
 const char* attn_strerror(int code) {
@@ -114,10 +279,14 @@ const char* attn_strerror(int code) {
     case ATTN_E_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case ATTN_E_ALIAS: return "an output overlaps an input or the other output";
     case ATTN_E_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case ATTN_E_FLAGS: return "unknown flag bits (only ATTN_CAUSAL is defined)";
+    case ATTN_E_SPLIT: return "number of key splits or split index out of range";
+    case ATTN_E_WORKSPACE:
+      return "workspace missing, too small, not 256-byte aligned or overlapping an argument";
     default: return "unknown error code";
   }
 }
 
-const char* attn_version(void) { return "0.1.0"; }
+const char* attn_version(void) { return "0.2.0"; }
 
 }  // extern "C"

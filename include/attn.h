@@ -23,9 +23,28 @@
  * probabilities are rounded to the input type before the second product.
  * O is written in the input type (round to nearest even); LSE in fp32.
  *
+ * Causal masking (attn_fwd_ex, flag ATTN_CAUSAL).  Query row i sees key j
+ * only if j <= i + (Lk - Lq): the diagonal is aligned to the end of both
+ * sequences, so the queries are the last Lq positions of the key sequence
+ * (with Lq = Lk the usual lower triangle).  The SyclKittens summary names
+ * partial-tile causal masking (section B.1.2) and causal runs with as few as
+ * 8 query rows against long key sequences (sections E.4, E.6), which only
+ * this alignment gives meaning.  A row that sees no key (Lq > Lk) has O = 0
+ * and LSE = -inf.
+ *
+ * Key splits (attn_fwd_ex with nsplit > 1, attn_fwd_partial, attn_merge).  The
+ * keys are cut into ranges; each range gives a partial result per row (its
+ * attention over that range alone and that range's LSE), and the partials
+ * merge exactly into the full result:
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) * O_s,
+ * the merge of online-softmax state of the SyclKittens summary, section I
+ * (context-parallel ring attention).  Splitting the keys gives short query
+ * sequences enough workgroups to fill the GPU (split-K of section E.2).
+ *
  * Layouts.  All tensors are contiguous and row-major with the head dimension
  * fastest:  Q, O: [B, Hq, Lq, D];  K, V: [B, Hkv, Lk, D];  LSE: [B, Hq, Lq].
- * Lq and Lk need not be multiples of any tile size.
+ * Partial results: O_part [nsplit, B, Hq, Lq, D] fp32, LSE_part
+ * [nsplit, B, Hq, Lq] fp32.  Lq and Lk need not be multiples of any tile size.
  *
  * Ownership.  Every pointer is device memory owned by the caller (for
  * example torch tensors).  The library never allocates, frees, retains or
@@ -46,8 +65,14 @@
 extern "C" {
 #endif
 
-/* Input/output element type. */
-typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+/* Input/output element type (ATTN_F32 only as the output type of attn_merge). */
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1, ATTN_F32 = 2 } attn_dtype_t;
+
+/* Flags of attn_fwd_ex / attn_fwd_partial / attn_plan_ex. */
+#define ATTN_CAUSAL 1u
+
+/* Largest number of key splits. */
+#define ATTN_MAX_SPLITS 256
 
 /* Return codes. */
 enum {
@@ -61,8 +86,13 @@ enum {
   ATTN_E_SCALE = -6,   /* scale is NaN or infinite */
   ATTN_E_ALIGN = -7,   /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   ATTN_E_ALIAS = -8,   /* o or lse overlaps an input, or lse overlaps o */
-  ATTN_E_LAUNCH = -9   /* the HIP runtime refused the launch (stream in an error state,
+  ATTN_E_LAUNCH = -9,  /* the HIP runtime refused the launch (stream in an error state,
                           invalid stream, no device) */
+  ATTN_E_FLAGS = -10,  /* a flag bit other than ATTN_CAUSAL is set */
+  ATTN_E_SPLIT = -11,  /* nsplit outside 0..ATTN_MAX_SPLITS (1..ATTN_MAX_SPLITS where a
+                          count is required), or a split index out of range */
+  ATTN_E_WORKSPACE = -12 /* workspace NULL, smaller than attn_workspace_bytes(), not
+                            256-byte aligned, or overlapping another argument */
 };
 
 /*
@@ -100,14 +130,101 @@ typedef struct {
   int32_t block_n;    /* keys per K/V tile */
   int32_t waves;      /* 64-lane wavefronts per workgroup */
   int32_t lds_bytes;  /* LDS per workgroup */
-  int64_t grid;       /* workgroups launched */
+  int64_t grid;       /* workgroups of the attention launch */
   char kernel[64];
+  int32_t nsplit;     /* key splits (1: no merge launch) */
+  int32_t split_len;  /* keys per split (the last one may be shorter) */
+  int64_t workspace_bytes; /* attn_workspace_bytes for nsplit */
 } attn_plan_t;
 
-/* Fill *plan for the given problem without launching anything (pure CPU).  Returns ATTN_OK
- * or the validation code for the shape/dtype arguments. */
+/* Fill *plan for the given problem without launching anything (pure CPU): the launch of
+ * attn_fwd (never split).  Returns ATTN_OK or the validation code for the shape/dtype
+ * arguments. */
 int attn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
               int in_dtype, attn_plan_t* plan);
+
+/* The launch attn_fwd_ex makes with nsplit = 0 and these flags: the planner picks the number
+ * of key splits from a cost model of the GPU's 256 compute units (one workgroup each), the
+ * key range per workgroup and the merge traffic. */
+int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                 int in_dtype, uint32_t flags, attn_plan_t* plan);
+
+/*
+ * attn_fwd_ex -- attn_fwd with options, on an explicit stream.
+ *   flags      0 or ATTN_CAUSAL
+ *   nsplit     1: one pass, as attn_fwd (workspace unused, may be NULL);
+ *              2..ATTN_MAX_SPLITS: the keys are cut into nsplit ranges (attn_split_range),
+ *              partial results go to the workspace and attn_merge combines them into o and
+ *              lse (two launches on `stream`);
+ *              0: the planner's choice (attn_plan_ex: more splits when the query tiles
+ *              alone would leave compute units idle).
+ *   workspace  device memory owned by the caller, 256-byte aligned, at least
+ *              attn_workspace_bytes(B, Hq, Lq, D, nsplit) bytes for the nsplit actually
+ *              used (query it with attn_plan_ex when passing 0); not retained after the
+ *              call's kernels finish.
+ * The result is the same as attn_fwd's up to rounding (the merge is exact in real
+ * arithmetic).  Returns ATTN_OK or a negative code; nothing is enqueued on error.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D, float scale,
+                int in_dtype, uint32_t flags, int64_t nsplit, void* workspace,
+                int64_t workspace_bytes, void* stream);
+
+/* attn_validate for attn_fwd_ex's arguments other than the workspace (pure CPU). */
+int attn_validate_ex(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                     int64_t D, float scale, int in_dtype, uint32_t flags, int64_t nsplit);
+
+/*
+ * attn_fwd_partial -- partial results over key ranges, one launch.
+ *   o_part    [nsplit, B, Hq, Lq, D] fp32 output: split s holds each row's attention over
+ *             the keys of attn_split_range(Lk, nsplit, s) alone (0 for a row that sees none)
+ *   lse_part  [nsplit, B, Hq, Lq] fp32 output: that range's natural-log sum of
+ *             exp(scale * q.k) (-inf for a row that sees no key of the range); required
+ *   nsplit    1..ATTN_MAX_SPLITS
+ * Other arguments as attn_fwd_ex.  o_part and lse_part must not overlap each other or the
+ * inputs; o_part 16-byte, lse_part 4-byte aligned.
+ */
+int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
+                     float* lse_part, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
+                     int64_t Lk, int64_t D, float scale, int in_dtype, uint32_t flags,
+                     int64_t nsplit, void* stream);
+
+/* attn_fwd_partial's argument check (pure CPU). */
+int attn_validate_partial(const void* q, const void* k, const void* v, const float* o_part,
+                          const float* lse_part, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
+                          int64_t Lk, int64_t D, float scale, int in_dtype, uint32_t flags,
+                          int64_t nsplit);
+
+/*
+ * attn_merge -- combine nsplit partial results per row into the full result.
+ *   o_part    [nsplit, rows, D] fp32;  lse_part [nsplit, rows] fp32 (natural log, -inf for
+ *             an empty part)
+ *   o         [rows, D] output of element type out_dtype (ATTN_F16, ATTN_BF16, ATTN_F32),
+ *             rounded to nearest even
+ *   lse       [rows] fp32 output, or NULL
+ *   D         a positive multiple of 8, at most 4096
+ * The inputs may come from attn_fwd_partial (rows = B*Hq*Lq) or from any source of
+ * partial attention results with this layout, e.g. key shards held elsewhere.  o_part and
+ * o 16-byte aligned, lse_part and lse 4-byte aligned; the outputs must not overlap the
+ * inputs or each other.  Returns ATTN_OK or a negative code.
+ */
+int attn_merge(const float* o_part, const float* lse_part, int64_t nsplit, int64_t rows,
+               int64_t D, void* o, float* lse, int out_dtype, void* stream);
+
+/* attn_merge's argument check (pure CPU). */
+int attn_validate_merge(const float* o_part, const float* lse_part, int64_t nsplit,
+                        int64_t rows, int64_t D, const void* o, const float* lse,
+                        int out_dtype);
+
+/* Key range [*begin, *end) of split s (0 <= s < nsplit) of Lk keys: ranges of
+ * ceil(ceil(Lk / nsplit) / 64) * 64 keys from key 0, the last ones cut at Lk or empty
+ * (begin = end = Lk).  Pure CPU.  Returns ATTN_OK, ATTN_E_SHAPE or ATTN_E_SPLIT. */
+int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int64_t* end);
+
+/* Workspace bytes attn_fwd_ex needs for nsplit splits (0 for nsplit = 1), or a negative
+ * code for bad sizes.  Layout: O_part at offset 0, LSE_part at the next 256-byte boundary. */
+int64_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t nsplit);
 
 /* Library version, "major.minor.patch". */
 const char* attn_version(void);

@@ -31,7 +31,9 @@ def declared_codes():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("attn_fwd", "attn_fwd_stream", "attn_validate", "attn_strerror", "attn_plan",
-                 "attn_version"):
+                 "attn_version", "attn_fwd_ex", "attn_validate_ex", "attn_fwd_partial",
+                 "attn_validate_partial", "attn_merge", "attn_validate_merge",
+                 "attn_split_range", "attn_workspace_bytes", "attn_plan_ex"):
         assert must in names, names
 
 
@@ -125,3 +127,129 @@ def test_plan_rejects_like_validate():
 
 def test_version():
     assert re.match(r"^\d+\.\d+\.\d+$", fa.attn_version())
+
+
+# ---- options: causal flag, key splits, partial results, merge ----
+
+def validate_ex(flags=0, nsplit=1, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.attn_validate_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                               a["Hkv"], a["Lq"], a["Lk"], a["D"], a["scale"], a["in_dtype"],
+                               flags, nsplit)
+
+
+def test_validate_ex():
+    assert validate_ex() == 0
+    assert validate_ex(flags=fa.ATTN_CAUSAL) == 0
+    assert validate_ex(nsplit=0) == 0 and validate_ex(nsplit=fa.ATTN_MAX_SPLITS) == 0
+    assert validate_ex(flags=2) == -10 and validate_ex(flags=0x80000000) == -10
+    assert validate_ex(nsplit=-1) == -11 and validate_ex(nsplit=fa.ATTN_MAX_SPLITS + 1) == -11
+    # the plain checks still run
+    assert validate_ex(flags=fa.ATTN_CAUSAL, D=64) == -3 and validate_ex(o=Q) == -8
+    # Lq > Lk is allowed under the causal mask (early rows are empty)
+    assert validate_ex(flags=fa.ATTN_CAUSAL, Lq=5000, Lk=100) == 0
+
+
+P_O, P_L = 11 * GB, 13 * GB
+
+
+def validate_partial(nsplit=4, flags=0, **over):
+    a = dict(GOOD, o_part=P_O, lse_part=P_L)
+    a.update(over)
+    return fa.attn_validate_partial(a["q"], a["k"], a["v"], a["o_part"], a["lse_part"], a["B"],
+                                    a["Hq"], a["Hkv"], a["Lq"], a["Lk"], a["D"], a["scale"],
+                                    a["in_dtype"], flags, nsplit)
+
+
+def test_validate_partial():
+    assert validate_partial() == 0 and validate_partial(nsplit=1, flags=fa.ATTN_CAUSAL) == 0
+    assert validate_partial(lse_part=None) == -1 and validate_partial(o_part=None) == -1
+    assert validate_partial(nsplit=0) == -11 and validate_partial(nsplit=257) == -11
+    assert validate_partial(flags=4) == -10
+    assert validate_partial(o_part=P_O + 4) == -7 and validate_partial(lse_part=P_L + 2) == -7
+    assert validate_partial(o_part=Q) == -8 and validate_partial(lse_part=K) == -8
+    # o_part of 4 splits: 4 * 32 * 4096 * 256 * 4 bytes = 0.5 GiB; lse_part just after is fine
+    pbytes = 4 * 32 * 4096 * 256 * 4
+    assert validate_partial(lse_part=P_O + pbytes) == 0
+    assert validate_partial(lse_part=P_O + pbytes - 4) == -8
+    assert validate_partial(D=100) == -3 and validate_partial(Hkv=5) == -4
+
+
+def validate_merge(nsplit=3, rows=1000, D=256, out_dtype=fa.ATTN_F16, **over):
+    a = dict(o_part=P_O, lse_part=P_L, o=O, lse=L)
+    a.update(over)
+    return fa.attn_validate_merge(a["o_part"], a["lse_part"], nsplit, rows, D, a["o"], a["lse"],
+                                  out_dtype)
+
+
+def test_validate_merge():
+    assert validate_merge() == 0 and validate_merge(lse=None) == 0
+    assert validate_merge(D=8, out_dtype=fa.ATTN_F32) == 0 and validate_merge(D=4096) == 0
+    assert validate_merge(o=None) == -1 and validate_merge(o_part=None) == -1
+    assert validate_merge(lse_part=None) == -1
+    assert validate_merge(nsplit=0) == -11 and validate_merge(nsplit=257) == -11
+    assert validate_merge(rows=0) == -2 and validate_merge(D=0) == -2
+    assert validate_merge(D=12) == -3 and validate_merge(D=4104) == -3
+    assert validate_merge(out_dtype=3) == -5 and validate_merge(out_dtype=-1) == -5
+    assert validate_merge(o=O + 8) == -7 and validate_merge(lse=L + 1) == -7
+    assert validate_merge(o_part=P_O + 4) == -7
+    assert validate_merge(o=P_O) == -8 and validate_merge(lse=P_L) == -8
+    assert validate_merge(lse=O + 4) == -8
+
+
+@pytest.mark.parametrize("Lk,nsplit", [(1, 1), (1, 5), (63, 2), (64, 2), (1000, 3),
+                                       (16384, 8), (16384, 7), (100, 4), (4096, 256)])
+def test_split_ranges_partition_the_keys(Lk, nsplit):
+    ranges = [fa.attn_split_range(Lk, nsplit, s) for s in range(nsplit)]
+    assert ranges[0][0] == 0 and ranges[-1][1] == Lk
+    for (b0, e0), (b1, e1) in zip(ranges[:-1], ranges[1:]):
+        assert e0 == b1 and b0 <= e0 <= b1 <= e1
+    if nsplit > 1:
+        # ranges of ceil(ceil(Lk / nsplit) / 64) * 64 keys from key 0, cut at Lk
+        n = -(-(-(-Lk // nsplit)) // 64) * 64
+        assert ranges == [(min(s * n, Lk), min(s * n + n, Lk)) for s in range(nsplit)]
+
+
+def test_split_range_errors():
+    for args, code in [((0, 1, 0), -2), ((10, 0, 0), -11), ((10, 2, 2), -11), ((10, 2, -1), -11),
+                       ((10, 257, 0), -11)]:
+        with pytest.raises(fa.AttnError) as e:
+            fa.attn_split_range(*args)
+        assert e.value.code == code
+
+
+def test_workspace_bytes():
+    assert fa.attn_workspace_bytes(1, 32, 1024, 256, 1) == 0
+    rows = 2 * 32 * 1000
+    o_bytes = -(-(4 * rows * 128 * 4) // 256) * 256
+    l_bytes = -(-(4 * rows * 4) // 256) * 256
+    assert fa.attn_workspace_bytes(2, 32, 1000, 128, 4) == o_bytes + l_bytes
+    assert fa.attn_workspace_bytes(1, 32, 1024, 256, 0) == -11
+    assert fa.attn_workspace_bytes(0, 32, 1024, 256, 2) == -2
+
+
+@pytest.mark.parametrize("shape,expect", [
+    ((1, 32, 2, 16384, 16384, 256), 1),   # 2048 workgroups: no split
+    ((4, 32, 2, 1024, 16384, 256), 1),    # 512 workgroups, two full rounds
+    ((1, 32, 2, 1024, 16384, 256), 2),    # 128 workgroups: half the CUs idle unsplit
+    ((1, 32, 2, 16, 16384, 256), 8),      # one query tile per head
+    ((1, 2, 1, 256, 256, 128), 1),        # too few keys to split
+])
+def test_plan_ex_split_choice(shape, expect):
+    p = fa.attn_plan_ex(*shape, fa.ATTN_F16, 0)
+    assert p.nsplit == expect
+    base = fa.attn_plan(*shape, fa.ATTN_F16)
+    assert p.grid == base.grid * p.nsplit
+    B, Hq, Hkv, Lq, Lk, D = shape
+    assert p.workspace_bytes == fa.attn_workspace_bytes(B, Hq, Lq, D, p.nsplit)
+    assert p.split_len == fa.attn_split_range(Lk, p.nsplit, 0)[1]
+    assert base.nsplit == 1 and base.workspace_bytes == 0
+
+
+def test_plan_ex_names_the_causal_kernel():
+    p = fa.attn_plan_ex(1, 8, 2, 512, 512, 128, fa.ATTN_BF16, fa.ATTN_CAUSAL)
+    assert p.kernel.decode() == "attn_fwd_d128_bf16_causal"
+    with pytest.raises(fa.AttnError) as e:
+        fa.attn_plan_ex(1, 8, 2, 512, 512, 128, fa.ATTN_BF16, 8)
+    assert e.value.code == -10

@@ -1,0 +1,179 @@
+"""GPU parity of the causal mask, the key-split path, the partial results and the merge
+kernel, through the C ABI, against the fp64 oracle.
+
+Causal: row i sees key j only if j <= i + Lk - Lq; rows that see no key (Lq > Lk) must
+come out as O = 0 and LSE = -inf exactly.  Splits: the merged result must meet the same
+tolerances as one pass; every partial must match the oracle's attention over its key
+range alone.  Every case prints its name, shape and seed before it touches the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs
+import flash_attention_amd as fa
+import oracle
+from parity_util import check, gpu_fwd, metrics, parity, scale_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(what):
+    print("\n[case] %s" % what, flush=True)
+
+
+def _causal_cases():
+    shapes = [  # B, Hq, Hkv, Lq, Lk
+        (1, 2, 1, 256, 256), (1, 4, 2, 300, 300), (1, 2, 1, 1024, 1024), (2, 4, 1, 97, 1000),
+        (1, 8, 2, 8, 4096), (1, 2, 2, 700, 300), (1, 2, 1, 513, 64), (1, 1, 1, 1, 1),
+        (1, 16, 1, 33, 33), (1, 4, 4, 1000, 1100),
+    ]
+    cases = []
+    i = 0
+    for D in (128, 256):
+        for dt in ("f16", "bf16"):
+            for sh in shapes:
+                cases.append((*sh, D, dt, 9000 + 10 * i))
+                i += 1
+    return cases
+
+
+CAUSAL = _causal_cases()
+
+
+@pytest.mark.parametrize("case", CAUSAL, ids=["B%d_H%d_%d_L%dx%d_D%d_%s_s%d" % c for c in CAUSAL])
+def test_causal_parity(case):
+    B, Hq, Hkv, Lq, Lk, D, dt, seed = case
+    _announce("causal " + str(case))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, dt, seed=seed)
+    parity(q, k, v, scale_of(D), dt, what="causal " + str(case), causal=True)
+
+
+@pytest.mark.parametrize("D,dt", [(128, "f16"), (256, "bf16")])
+def test_causal_first_row_is_exact(D, dt):
+    """Lq = Lk: row 0 sees key 0 alone, so its weight is exactly 1 and O equals V_0 bit
+    for bit; the last row sees every key and equals the unmasked result bit for bit."""
+    _announce("causal first/last row D=%d %s" % (D, dt))
+    q, k, v = attn_inputs.make_qkv(1, 4, 2, 300, 300, D, dt, seed=21)
+    o, lse = gpu_fwd(q, k, v, scale_of(D), causal=True)
+    v_rep = v.repeat_interleave(2, dim=1)
+    assert torch.equal(o[:, :, 0], v_rep[:, :, 0])
+    s0 = (q[:, :, 0].double() * k.repeat_interleave(2, dim=1)[:, :, 0].double()).sum(-1)
+    assert torch.allclose(lse[:, :, 0].double(), s0 * float(np.float32(scale_of(D))), atol=1e-4)
+    o_full, lse_full = gpu_fwd(q, k, v, scale_of(D))
+    assert torch.equal(o[:, :, -1], o_full[:, :, -1])
+    assert torch.equal(lse[:, :, -1], lse_full[:, :, -1])
+
+
+def test_causal_empty_rows_exact():
+    """Lq > Lk: the first Lq - Lk rows see no key: O = 0 and LSE = -inf, bit for bit."""
+    _announce("causal empty rows")
+    q, k, v = attn_inputs.make_qkv(1, 4, 2, 600, 100, 256, "f16", seed=22)
+    o, lse = gpu_fwd(q, k, v, scale_of(256), causal=True)
+    assert torch.equal(o[:, :, :500], torch.zeros_like(o[:, :, :500]))
+    assert bool(torch.all(lse[:, :, :500] == -math.inf))
+    assert bool(torch.isfinite(lse[:, :, 500:]).all())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_causal_and_split_deterministic(causal):
+    _announce("determinism causal=%s nsplit=3" % causal)
+    q, k, v = attn_inputs.make_qkv(1, 8, 2, 700, 2000, 256, "f16", seed=23)
+    o1, l1 = gpu_fwd(q, k, v, scale_of(256), causal=causal, nsplit=3)
+    o2, l2 = gpu_fwd(q, k, v, scale_of(256), causal=causal, nsplit=3)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _split_cases():
+    cases = []
+    i = 0
+    for (B, Hq, Hkv, Lq, Lk) in [(1, 4, 2, 200, 1000), (2, 2, 1, 64, 3000), (1, 8, 8, 300, 700),
+                                 (1, 2, 1, 1000, 129), (1, 4, 1, 16, 4096)]:
+        for D, dt in ((128, "bf16"), (256, "f16")):
+            for nsplit in (2, 5, 0):
+                for causal in (False, True):
+                    cases.append((B, Hq, Hkv, Lq, Lk, D, dt, nsplit, causal, 9500 + i))
+                    i += 1
+    return cases
+
+
+SPLIT = _split_cases()
+
+
+@pytest.mark.parametrize("case", SPLIT,
+                         ids=["B%d_H%d_%d_L%dx%d_D%d_%s_ns%d_c%d_s%d" % c for c in SPLIT])
+def test_split_parity(case):
+    B, Hq, Hkv, Lq, Lk, D, dt, nsplit, causal, seed = case
+    _announce("split " + str(case))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, dt, seed=seed)
+    parity(q, k, v, scale_of(D), dt, what="split " + str(case), causal=causal, nsplit=nsplit)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nsplit", [1, 3, 40])
+def test_partials_match_oracle_ranges(nsplit, causal):
+    """Each split's partial result is the oracle's attention over that key range alone
+    (key positions global, so the causal diagonal stays put); splits past the end, or past
+    a row's diagonal, are empty (O = 0, LSE = -inf)."""
+    B, Hq, Hkv, Lq, Lk, D = 1, 4, 2, 300, 1000, 128
+    _announce("partials nsplit=%d causal=%s" % (nsplit, causal))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "f16", seed=24)
+    scale = float(np.float32(scale_of(D)))
+    dev = torch.device("cuda:0")
+    o_part, lse_part = fa.fwd_partial(q.to(dev), k.to(dev), v.to(dev), nsplit, scale=scale,
+                                      causal=causal)
+    torch.cuda.synchronize()
+    o_part, lse_part = o_part.cpu(), lse_part.cpu()
+    for s in range(nsplit):
+        b, e = fa.attn_split_range(Lk, nsplit, s)
+        if b == e:
+            assert not o_part[s].any() and bool(torch.all(lse_part[s] == -math.inf)), s
+            continue
+        o_ref, lse_ref = oracle.attention(q, k[:, :, b:e].contiguous(), v[:, :, b:e].contiguous(),
+                                          scale, causal=causal, key_begin=b, lk_total=Lk)
+        m = metrics(o_part[s].reshape(-1, D), lse_part[s].reshape(-1), o_ref, lse_ref)
+        print("[partial] split %d [%d,%d) %s" % (s, b, e, m), flush=True)
+        check(m, "f16", "partial %d" % s)
+
+
+@pytest.mark.parametrize("D,out", [(128, torch.float16), (256, torch.bfloat16),
+                                   (8, torch.float32), (136, torch.float32)])
+def test_merge_kernel_matches_oracle(D, out):
+    """Random partials (LSE spread over +-30, some parts empty, one row empty in every
+    part) merged on the GPU against the oracle's fp64 merge."""
+    _announce("merge D=%d out=%s" % (D, out))
+    P, rows = 5, 3001
+    g = torch.Generator().manual_seed(25)
+    o_part = torch.randn(P, rows, D, generator=g)
+    lse_part = torch.rand(P, rows, generator=g) * 60 - 30
+    lse_part[1, ::3] = -math.inf  # empty parts carry no weight
+    lse_part[:, 7] = -math.inf    # a row empty in every part
+    o_part[:, 7] = 0
+    dev = torch.device("cuda:0")
+    o, lse = fa.merge(o_part.to(dev), lse_part.to(dev), out_dtype=out)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.merge(o_part.double().numpy(), lse_part.double().numpy())
+    og = o.cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    assert not og[7].any() and lg[7] == -math.inf
+    fin = np.isfinite(lse_ref)
+    assert np.isfinite(lg[fin]).all() and np.isfinite(og).all()
+    # fp32 arithmetic, then rounding to the output type
+    tol = {torch.float32: 2e-6, torch.float16: 2e-3, torch.bfloat16: 1.6e-2}[out]
+    err = np.abs(og - o_ref).max()
+    assert err <= tol * max(1.0, np.abs(o_ref).max()), err
+    assert np.abs(lg[fin] - lse_ref[fin]).max() <= 1e-5 * 30, np.abs(lg[fin] - lse_ref[fin]).max()
+
+
+def test_merge_without_lse_and_single_part():
+    """lse = NULL leaves no LSE; one part merges to itself (weight exactly 1)."""
+    _announce("merge single part")
+    g = torch.Generator().manual_seed(26)
+    o_part = torch.randn(1, 100, 64, generator=g)
+    lse_part = torch.randn(1, 100, generator=g)
+    dev = torch.device("cuda:0")
+    o, lse = fa.merge(o_part.to(dev), lse_part.to(dev), lse=False)
+    torch.cuda.synchronize()
+    assert lse is None and torch.equal(o.cpu(), o_part[0])

@@ -15,23 +15,28 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "flash_attention_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "flash_attention_amd", "csrc")
+SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_merge.hip")]
 
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    out = str(tmp_path_factory.mktemp("asm") / "attn_fwd.s")
-    cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
-           "-I" + os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "--cuda-device-only", "-S", SRC, "-o", out]
-    subprocess.run(cmd, check=True, capture_output=True)
-    return open(out).read()
+    text = []
+    for src in SOURCES:
+        out = str(tmp_path_factory.mktemp("asm") / (os.path.basename(src) + ".s"))
+        cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
+               "-I" + os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang",
+               "-packed-fp32-ops", "--cuda-device-only", "-S", src, "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True)
+        text.append(open(out).read())
+    return "\n".join(text)
 
 
-def kernels(text):
+def kernels(text, which="attn_(?:fwd|merge)_kernel"):
     """{kernel symbol: list of instruction lines with an in_asm flag}."""
     res = {}
-    for m in re.finditer(r"^(_Z\w*attn_fwd_kernel\w*):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
+    pat = r"^(_Z\w*%s\w*):[^\n]*\n(.*?)^\s*s_endpgm" % which
+    for m in re.finditer(pat, text, re.M | re.S):
         lines, inside = [], False
         for ln in m.group(2).splitlines():
             s = ln.strip()
@@ -46,8 +51,9 @@ def kernels(text):
 
 
 def test_all_kernels_present(asm):
-    ks = kernels(asm)
+    ks = kernels(asm, "attn_fwd_kernel")
     assert len(ks) == 8, sorted(ks)  # D in {128,256} x {f16,bf16} x scale sign
+    assert len(kernels(asm, "attn_merge_kernel")) == 3  # output fp16, bf16, fp32
 
 
 def test_no_agpr_outside_inline_asm(asm):

@@ -59,7 +59,7 @@ def test_parity_workload_full_size(name):
     _announce("%s %s" % (name, w.describe()))
     q, k, v = attn_inputs.workload_qkv(w)
     rows = None if name == "tiny" else attn_inputs.sample_rows(w)
-    parity(q, k, v, w.scale, w.dtype, rows=rows, what=name)
+    parity(q, k, v, w.scale, w.dtype, rows=rows, what=name, causal=w.causal, nsplit=w.nsplit)
 
 
 def test_worked_example_on_gpu():
