@@ -571,46 +571,53 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         vf[1] = vfrag_load(VST, 1);
       }
     });
+    // Each P.V step is two half-steps: one MFMA (query block qb), then a slice of VALU or
+    // copy work that issues while that MFMA runs.  A wave issues in order, so work placed
+    // after an MFMA overlaps it only until the next MFMA: one half-step per MFMA gives
+    // every MFMA its own window.  Exponentials (quarter-rate) are spread one or two per
+    // window over all half-steps after the first.
+    constexpr int H = 2 * NSTEP;                  // half-steps
+    constexpr int EXP0 = PV ? 1 : 3;              // first half-step with exponentials
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if constexpr (PV) {
         if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(VST, s + 2);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pprev[qb][s & 1]);
       }
-      if (s == 0) {
-        mfma_fence_v(sacc[0], sacc[1]);
-        mask_keys(sacc, t);
-        if (!PV) row_max(sacc, 0);  // tile 0 only: it fixes the reference
-      } else if (s == 1) {
-        if (!PV) row_max(sacc, 1);
-      } else if (s == 2) {
-        if (!PV) {
+#pragma unroll
+      for (int hb = 0; hb < QB; ++hb) {
+        const int h = 2 * s + hb;
+        if constexpr (PV) Elt<T>::acc_mfma(hb * DB + (s >> 1), vf[s % 3], pprev[hb][s & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (h == 0) {
+          mfma_fence_v(sacc[0], sacc[1]);
+          mask_keys(sacc, t);
+          if (!PV) row_max(sacc, 0);  // tile 0 only: it fixes the reference
+        } else if (!PV && h == 1) {
+          row_max(sacc, 1);
+        } else if (!PV && h == 2) {
           set_reference();
           finite_reference();
         }
-      } else {
-        // the 32 exponentials spread over steps 3..NSTEP-1
-        exp_slice(sacc, pcur, 32 * (s - 3) / (NSTEP - 3), 32 * (s - 2) / (NSTEP - 3));
-      }
-      if (s == SYNC_STEP) sync_point(t);
-      // copies of tile t+2, one wave per step after the synchronisation point, so that the
-      // four waves' copies do not queue up behind each other
-      static_assert(SYNC_STEP + attn_cfg::kWaves == NSTEP, "one copy step per wave");
-      if (s >= SYNC_STEP && t + 2 < ntiles && wave == s - SYNC_STEP)
-        issue_tile(t + 2, (ST + 2) % NSTAGE);
-      if (s == NSTEP - 1) {
+        if (h >= EXP0)
+          exp_slice(sacc, pcur, 32 * (h - EXP0) / (H - EXP0), 32 * (h - EXP0 + 1) / (H - EXP0));
+        if (h == 2 * SYNC_STEP) sync_point(t);
+        // copies of tile t+2, one wave per step after the synchronisation point, so that
+        // the four waves' copies do not queue up behind each other
+        static_assert(SYNC_STEP + attn_cfg::kWaves == NSTEP, "one copy step per wave");
+        if (hb == QB - 1 && s >= SYNC_STEP && t + 2 < ntiles && wave == s - SYNC_STEP)
+          issue_tile(t + 2, (ST + 2) % NSTAGE);
+        if (h == H - 1) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
-        if (PV && !exact_m) check_growth();
-        if (t + 1 < ntiles) {
-          // first two K fragments of tile t+1 (landed at the sync point)
-          kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
-          kf[1] = kfrag(kstage((ST + 1) % NSTAGE), 1);
+          for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
+          if (PV && !exact_m) check_growth();
+          if (t + 1 < ntiles) {
+            // first two K fragments of tile t+1 (landed at the sync point)
+            kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
+            kf[1] = kfrag(kstage((ST + 1) % NSTAGE), 1);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // P.V of the last tile (no softmax, no synchronisation).
