@@ -559,10 +559,9 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   u32x4 kf[3];
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
   auto iteration = [&](auto pv_tag, auto st_tag, int t, u32x4 (&pprev)[QB][2],
-                       u32x4 (&pcur)[QB][2]) {
+                       u32x4 (&pcur)[QB][2], f32x16 (&sacc)[QB]) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
-    f32x16 sacc[QB];
     constexpr int VST = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
     u32x4 vf[3];
     qk(kstage(ST), sacc, kf, [&]() {
@@ -576,6 +575,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     // after an MFMA overlaps it only until the next MFMA: one half-step per MFMA gives
     // every MFMA its own window.  Exponentials (quarter-rate) are spread one or two per
     // window over all half-steps after the first.
+    // (the wave index laundered per iteration: the compiler would otherwise keep one
+    // loop-invariant lane mask per copy step, and spill them)
+    int wv = wave;
+    asm volatile("" : "+s"(wv));
     constexpr int H = 2 * NSTEP;                  // half-steps
     constexpr int EXP0 = PV ? 1 : 3;              // first half-step with exponentials
 #pragma unroll
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         // copies of tile t+2, one wave per step after the synchronisation point, so that
         // the four waves' copies do not queue up behind each other
         static_assert(SYNC_STEP + attn_cfg::kWaves == NSTEP, "one copy step per wave");
-        if (hb == QB - 1 && s >= SYNC_STEP && t + 2 < ntiles && wave == s - SYNC_STEP)
+        if (hb == QB - 1 && s >= SYNC_STEP && t + 2 < ntiles && wv == s - SYNC_STEP)
           issue_tile(t + 2, (ST + 2) % NSTAGE);
         if (h == H - 1) {
 #pragma unroll
@@ -673,6 +676,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // four: the stage of each iteration is a compile-time constant and the two P buffers
   // swap roles without copies.
   u32x4 pa[QB][2], pb2[QB][2];
+  f32x16 sacc[QB];  // scores of the current tile
   // (a workgroup with no key to look at, under the causal mask or past the last split,
   // skips the loop: its rows are empty)
   if (ntiles > 0) for (;;) {
@@ -685,16 +689,16 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
-    iteration(std::false_type{}, S0{}, 0, pb2, pa);
+    iteration(std::false_type{}, S0{}, 0, pb2, pa, sacc);
     int t = 1;
     while (t < ntiles) {  // P(t-1) in pa for odd t, in pb2 for even t
-      iteration(std::true_type{}, S1{}, t, pa, pb2);
+      iteration(std::true_type{}, S1{}, t, pa, pb2, sacc);
       if (++t >= ntiles) break;
-      iteration(std::true_type{}, S2{}, t, pb2, pa);
+      iteration(std::true_type{}, S2{}, t, pb2, pa, sacc);
       if (++t >= ntiles) break;
-      iteration(std::true_type{}, S3{}, t, pa, pb2);
+      iteration(std::true_type{}, S3{}, t, pa, pb2, sacc);
       if (++t >= ntiles) break;
-      iteration(std::true_type{}, S0{}, t, pb2, pa);
+      iteration(std::true_type{}, S0{}, t, pb2, pa, sacc);
       ++t;
     }
     // Did any wave see its scores outgrow the reference?  (The writer waits for its flag
