@@ -74,6 +74,11 @@ WORKLOADS = {
                                    seed_base=6000, causal=True),
     "q1kx16k_d256_split": Workload("q1kx16k_d256_split", 1, 32, 2, 1024, 16384, 256, "f16",
                                    seed_base=7000, nsplit=0),
+    # decode-like: 16 new queries per sequence (the last 16 positions, causal) against 16K
+    # keys, 4 sequences: the 16 query heads of a key/value head share its workgroups' rows
+    # and the planner splits the keys
+    "decode16x16k_d256": Workload("decode16x16k_d256", 4, 32, 2, 16, 16384, 256, "f16",
+                                  seed_base=8000, causal=True, nsplit=0),
 }
 HEADLINE = "gqa16k_d256"
 

@@ -68,6 +68,13 @@ struct Params {
   int split_len;  // keys per split, a multiple of the key tile (split s: [s*len, (s+1)*len))
   int diag;       // row i sees key j only if j <= i + diag (Lk - Lq if causal, else Lk)
   int causal;     // heaviest query tiles first (their key range is the longest)
+  // Query position of row r: r % lq_head.  The host passes the G query heads that share a
+  // key/value head as one block of G*Lq rows (Hq = Hkv, G = 1 here), so a row's position
+  // in its own head is its index modulo the per-head length; floor(r / lq_head) =
+  // (r * lq_magic) >> lq_shift exactly for 0 <= r < 2^31.
+  int lq_head;
+  uint32_t lq_magic;
+  int lq_shift;
   float c;        // scale * log2(e): scores are kept in base-2 units
 };
 
@@ -259,13 +266,31 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   const int b = __builtin_amdgcn_readfirstlane(bh / p.Hq);
   const int hkv = __builtin_amdgcn_readfirstlane(hq / p.G);
 
+  // Position of row r in its head's query sequence (rows of several heads may share a
+  // workgroup or a wavefront).
+  auto pos_of = [&](int r) {
+    const int hd = static_cast<int>((static_cast<uint64_t>(static_cast<uint32_t>(r)) *
+                                     p.lq_magic) >> p.lq_shift);
+    return r - hd * p.lq_head;
+  };
+  // Largest position among rows first..last: the last row's, unless they cross into the
+  // next head (then some row is its head's last).
+  auto max_pos = [&](int first, int last) {
+    return pos_of(first) + (last - first) >= p.lq_head ? p.lq_head - 1 : pos_of(last);
+  };
+  // Smallest position among rows first..last.
+  auto min_pos = [&](int first, int last) {
+    return pos_of(first) + (last - first) >= p.lq_head ? 0 : pos_of(first);
+  };
+
   // Keys of this workgroup: its split [kbeg, kbeg + split_len), cut at Lk and, under the
-  // causal mask, after the last key its last query row sees.  Tile t holds keys
+  // causal mask, after the last key its rows see.  Tile t holds keys
   // kbeg + 32t .. kbeg + 32t + 31.
   const int Lk = p.Lk;
   const int kbeg = min(split * p.split_len, Lk);
   const int qlast = min(qtile * BM + BM - 1, p.Lq - 1);
-  const int kend = min(min(Lk, kbeg + p.split_len), qlast + p.diag + 1);
+  const int imax = __builtin_amdgcn_readfirstlane(max_pos(qtile * BM, qlast));
+  const int kend = min(min(Lk, kbeg + p.split_len), imax + p.diag + 1);
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
   const int nfull = (Lk - kbeg) / BN;  // tiles whose 32 rows all exist in K and V
 
@@ -278,7 +303,8 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // masks.
   const int key_lim = Lk - 1 - kbeg;
   const int row_off = p.diag - kbeg;
-  const int wave_lim = min(key_lim, qrow0 + row_off);
+  const int wave_lim =
+      min(key_lim, __builtin_amdgcn_readfirstlane(min_pos(qrow0, qrow0 + 32 * QB - 1)) + row_off);
 
   // ---- direct HBM->LDS copies of K and V tiles ----
   // Copy round i of this thread moves tile row r = i*ROWS_PER_LOAD + r0, 16-byte chunk c0
@@ -468,7 +494,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int row = qrow0 + qb * 32 + (ln & 31);
-        const int lim = min(key_lim, row + row_off) - tt * BN - 4 * (ln >> 5);
+        const int lim = min(key_lim, pos_of(row) + row_off) - tt * BN - 4 * (ln >> 5);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + (r & 3) > lim) sacc[qb][r] = kWorst;
@@ -811,12 +837,25 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
   prm.o_part = o_part;
   prm.lse_part = lse_part;
   prm.part_rows = B * Hq * Lq;
-  prm.Hq = static_cast<int>(Hq);
+  // The G query heads of each key/value head are adjacent in Q, O and LSE, so they are
+  // handed to the kernel as one head of G*Lq rows: short query sequences still fill the
+  // workgroups' rows.  Addresses are unchanged; only the causal mask needs a row's own
+  // position (row % Lq).
+  const int64_t G = Hq / Hkv;
+  prm.Hq = static_cast<int>(Hkv);
   prm.Hkv = static_cast<int>(Hkv);
-  prm.G = static_cast<int>(Hq / Hkv);
-  prm.Lq = static_cast<int>(Lq);
+  prm.G = 1;
+  prm.Lq = static_cast<int>(G * Lq);
   prm.Lk = static_cast<int>(Lk);
-  prm.n_qtiles = static_cast<int>((Lq + block_m - 1) / block_m);
+  prm.n_qtiles = static_cast<int>((G * Lq + block_m - 1) / block_m);
+  prm.lq_head = static_cast<int>(Lq);
+  {
+    int l = 0;
+    while ((int64_t(1) << l) < Lq) ++l;
+    const uint64_t two = uint64_t(1) << (31 + l);
+    prm.lq_magic = static_cast<uint32_t>((two + static_cast<uint64_t>(Lq) - 1) / Lq);
+    prm.lq_shift = 31 + l;
+  }
   prm.nsplit = static_cast<int>(nsplit);
   int64_t b0 = 0, e0 = Lk;
   attn_split_range(Lk, nsplit, 0, &b0, &e0);

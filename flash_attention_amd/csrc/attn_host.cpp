@@ -24,6 +24,16 @@ struct PlanInternal {
   int qb, bn, stages, block_m, lds;
 };
 
+bool plan_for_d(int64_t D, PlanInternal* p);
+
+// Workgroups per batch entry and key split: the G = Hq/Hkv query heads of a key/value head
+// are one block of G*Lq query rows (adjacent in memory), cut into tiles of block_m rows.
+int64_t query_tiles(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D) {
+  PlanInternal p;
+  plan_for_d(D, &p);
+  return (Hq / Hkv * Lq + p.block_m - 1) / p.block_m * Hkv;
+}
+
 bool plan_for_d(int64_t D, PlanInternal* p) {
   using namespace attn_cfg;
   if (D == 128) {
@@ -51,11 +61,11 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int6
   const int64_t lim = (int64_t(1) << 31) - 1;
   if (Lq > lim / D || Lk > lim / D) return ATTN_E_SHAPE;  // per-head offsets fit in int32
   if (B > lim || Hq > lim) return ATTN_E_SHAPE;
-  PlanInternal p;
-  plan_for_d(D, &p);
-  const int64_t qtiles = (Lq + p.block_m - 1) / p.block_m;
-  if (qtiles > lim / Hq || qtiles * Hq > lim / B) return ATTN_E_SHAPE;  // grid < 2^31
-  if (qtiles * Hq * B > lim / nsplit) return ATTN_E_SHAPE;
+  // the query heads of one key/value head run as one block of G*Lq rows: its row offsets
+  // fit in int32 too
+  if (Hq / Hkv > lim / D / Lq) return ATTN_E_SHAPE;
+  const int64_t groups = query_tiles(Hq, Hkv, Lq, D);  // workgroups per (b, split)
+  if (groups > lim / B || groups * B > lim / nsplit) return ATTN_E_SHAPE;  // grid < 2^31
   return ATTN_OK;
 }
 
@@ -72,12 +82,12 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 // runs one workgroup per compute unit (256 of them); a workgroup costs its key tiles plus
 // a fixed overhead for pipeline fill, drain and epilogue; splitting adds the partial
 // results' round trip through HBM and a second launch.
-double split_cost(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int64_t D, int64_t ns,
-                  int block_m) {
+double split_cost(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                  int64_t ns, int block_m) {
   constexpr double kCUs = 256, kOverheadTiles = 4, kLaunchTiles = 3;
   const int64_t len = split_len_of(Lk, ns);
   const int64_t used = (Lk + len - 1) / len;  // splits with keys
-  const int64_t wg = (Lq + block_m - 1) / block_m * Hq * B * used;
+  const int64_t wg = (Hq / Hkv * Lq + block_m - 1) / block_m * Hkv * B * used;
   const double rounds = std::ceil(static_cast<double>(wg) / kCUs);
   double cost = rounds * (static_cast<double>(len) / 32.0 + kOverheadTiles);
   if (ns > 1) {
@@ -90,13 +100,13 @@ double split_cost(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int64_t D, int6
   return cost;
 }
 
-int64_t choose_nsplit(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int64_t D,
+int64_t choose_nsplit(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                       int block_m) {
   int64_t best = 1;
-  double best_cost = split_cost(B, Hq, Lq, Lk, D, 1, block_m);
-  for (int64_t ns = 2; ns <= 32; ++ns) {
-    if (split_len_of(Lk, ns) < 512) break;  // splits shorter than 16 tiles do not pay
-    const double c = split_cost(B, Hq, Lq, Lk, D, ns, block_m);
+  double best_cost = split_cost(B, Hq, Hkv, Lq, Lk, D, 1, block_m);
+  for (int64_t ns = 2; ns <= 128; ++ns) {
+    if (split_len_of(Lk, ns) < 256) break;  // splits shorter than 8 tiles do not pay
+    const double c = split_cost(B, Hq, Hkv, Lq, Lk, D, ns, block_m);
     if (c < 0.95 * best_cost) {  // a split must win clearly
       best = ns;
       best_cost = c;
@@ -114,15 +124,15 @@ const char* kernel_name(int64_t D, int in_dtype, uint32_t flags) {
                               : (c ? "attn_fwd_d256_bf16_causal" : "attn_fwd_d256_bf16");
 }
 
-int fill_plan(int64_t B, int64_t Hq, int64_t Lq, int64_t Lk, int64_t D, int in_dtype,
-              uint32_t flags, int64_t nsplit, attn_plan_t* plan) {
+int fill_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+              int in_dtype, uint32_t flags, int64_t nsplit, attn_plan_t* plan) {
   PlanInternal p;
   plan_for_d(D, &p);
   plan->block_m = p.block_m;
   plan->block_n = p.bn;
   plan->waves = attn_cfg::kWaves;
   plan->lds_bytes = p.lds;
-  plan->grid = ((Lq + p.block_m - 1) / p.block_m) * Hq * B * nsplit;
+  plan->grid = query_tiles(Hq, Hkv, Lq, D) * B * nsplit;
   std::memset(plan->kernel, 0, sizeof plan->kernel);
   std::strncpy(plan->kernel, kernel_name(D, in_dtype, flags), sizeof plan->kernel - 1);
   plan->nsplit = static_cast<int32_t>(nsplit);
@@ -251,7 +261,7 @@ int attn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_
   if (!plan) return ATTN_E_NULLPTR;
   int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype);
   if (rc != ATTN_OK) return rc;
-  return fill_plan(B, Hq, Lq, Lk, D, in_dtype, 0, 1, plan);
+  return fill_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, 0, 1, plan);
 }
 
 int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
@@ -262,9 +272,9 @@ int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int
   if (rc != ATTN_OK) return rc;
   PlanInternal p;
   plan_for_d(D, &p);
-  int64_t ns = choose_nsplit(B, Hq, Lq, Lk, D, p.block_m);
+  int64_t ns = choose_nsplit(B, Hq, Hkv, Lq, Lk, D, p.block_m);
   while (ns > 1 && check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, ns) != ATTN_OK) --ns;
-  return fill_plan(B, Hq, Lq, Lk, D, in_dtype, flags, ns, plan);
+  return fill_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, ns, plan);
 }
 
 const char* attn_strerror(int code) {

@@ -99,8 +99,11 @@ def test_validate_rejects(over, code):
 
 
 def test_validate_grid_limit():
-    # a grid of 2^31 or more workgroups is refused, not truncated
-    assert validate(B=1 << 20, Hq=1 << 11, Hkv=1, Lq=128, Lk=128) == -2
+    # a grid of 2^31 or more workgroups is refused, not truncated: 2^21 batches of one
+    # key/value head with 2048 query heads x 128 rows (1024 tiles of 256 rows)
+    assert validate(B=1 << 21, Hq=1 << 11, Hkv=1, Lq=128, Lk=128) == -2
+    # the query rows of one key/value group (Hq/Hkv * Lq) * D stay below 2^31
+    assert validate(Hq=256, Hkv=1, Lq=(1 << 31) // 256 // 256 + 1, Lk=64) == -2
 
 
 def test_lse_may_follow_o_directly():
@@ -114,7 +117,8 @@ def test_lse_may_follow_o_directly():
 def test_plan(D, dtype):
     p = fa.attn_plan(2, 8, 2, 1000, 777, D, dtype)
     assert p.waves >= 1 and p.block_m % 32 == 0 and p.block_n % 32 == 0
-    assert p.grid == math.ceil(1000 / p.block_m) * 8 * 2
+    # the 4 query heads of each key/value head form one block of 4000 rows
+    assert p.grid == math.ceil(4 * 1000 / p.block_m) * 2 * 2
     assert 0 < p.lds_bytes <= 160 * 1024
     assert p.kernel.decode().startswith("attn_fwd_d%d" % D)
 
@@ -230,15 +234,15 @@ def test_workspace_bytes():
 
 
 @pytest.mark.parametrize("shape,expect", [
-    ((1, 32, 2, 16384, 16384, 256), 1),   # 2048 workgroups: no split
-    ((4, 32, 2, 1024, 16384, 256), 1),    # 512 workgroups, two full rounds
-    ((1, 32, 2, 1024, 16384, 256), 2),    # 128 workgroups: half the CUs idle unsplit
-    ((1, 32, 2, 16, 16384, 256), 8),      # one query tile per head
-    ((1, 2, 1, 256, 256, 128), 1),        # too few keys to split
+    ((1, 32, 2, 16384, 16384, 256), (1, 1)),    # 2048 workgroups: no split
+    ((4, 32, 2, 1024, 16384, 256), (1, 1)),     # 512 workgroups, two full rounds
+    ((1, 32, 2, 1024, 16384, 256), (2, 2)),     # 128 workgroups: half the CUs idle unsplit
+    ((1, 32, 2, 16, 16384, 256), (32, 64)),     # decode: 2 workgroups (16 heads x 16 rows each)
+    ((1, 2, 1, 256, 256, 128), (1, 1)),         # too few keys to split
 ])
 def test_plan_ex_split_choice(shape, expect):
     p = fa.attn_plan_ex(*shape, fa.ATTN_F16, 0)
-    assert p.nsplit == expect
+    assert expect[0] <= p.nsplit <= expect[1], p.nsplit
     base = fa.attn_plan(*shape, fa.ATTN_F16)
     assert p.grid == base.grid * p.nsplit
     B, Hq, Hkv, Lq, Lk, D = shape
