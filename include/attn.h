@@ -79,7 +79,8 @@ enum {
   ATTN_OK = 0,
   ATTN_E_NULLPTR = -1, /* q, k, v or o is NULL (lse may be NULL: LSE is then not written) */
   ATTN_E_SHAPE = -2,   /* B, Hq, Hkv, Lq or Lk <= 0, or a size past the supported range:
-                          Lq*D and Lk*D must stay below 2^31, the grid below 2^31 blocks */
+                          Lq*D, (Hq/Hkv)*Lq*D and Lk*D must stay below 2^31, the grid
+                          below 2^31 blocks */
   ATTN_E_HEADDIM = -3, /* D is not 128 or 256 */
   ATTN_E_GQA = -4,     /* Hq is not a multiple of Hkv */
   ATTN_E_DTYPE = -5,   /* in_dtype is neither ATTN_F16 nor ATTN_BF16 */
