@@ -1,9 +1,9 @@
 // attn_config.h -- tile shapes shared by the planner (host) and the kernels (device).
 //
 // One workgroup = kWaves wavefronts of 64 lanes, one wavefront per SIMD.  Each wavefront
-// owns 32*QB query rows of one query head for the whole key sequence, so the online
-// softmax never needs a cross-wave reduction.  Keys stream through LDS in tiles of BN
-// rows, STAGES tiles in flight.
+// owns 32*QB whole query rows for the workgroup's whole key range, so the online softmax
+// never needs a cross-wave reduction.  Keys stream through LDS in tiles of BN rows,
+// STAGES tiles in flight.
 #pragma once
 
 namespace attn_cfg {
@@ -30,7 +30,8 @@ struct Tile<256> {
 
 constexpr int block_m(int qb) { return kWaves * 32 * qb; }
 
-// STAGES x (K tile + V tile), each [BN][D] 16-bit elements, plus two restart flags.
+// STAGES x (K tile + V tile), each [BN][D] 16-bit elements, plus the restart flag (16
+// bytes reserved).
 constexpr int lds_bytes(int d, int bn, int stages) { return stages * 2 * bn * d * 2 + 16; }
 
 }  // namespace attn_cfg

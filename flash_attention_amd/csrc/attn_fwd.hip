@@ -8,17 +8,21 @@
 // data-flow diagram).  The Xe2 register and SLM choreography is not reused; the layout
 // below is built around CDNA4's 32x32x16 MFMA.
 //
-// Work decomposition.  A workgroup is 4 wavefronts and owns BLOCK_M = 128*QB query rows of
-// one query head; each wavefront owns 32*QB whole rows, so a row's max and sum never cross
-// wavefronts.  The grouped-query head map (query head h reads key/value head h / (Hq/Hkv))
-// is resolved from the block index.
+// Work decomposition.  The G = Hq/Hkv query heads that read one key/value head are
+// adjacent in Q, O and LSE, so the host hands them over as one block of G*Lq query rows
+// (the grouped-query head map h -> h / G becomes row block -> key/value head).  A workgroup
+// is 4 wavefronts and owns BLOCK_M = 128*QB rows of such a block and one range of keys
+// (the whole sequence, or one split of it); each wavefront owns 32*QB whole rows, so a
+// row's max and sum never cross wavefronts.  Under the causal mask a row's position in
+// its own head is its index modulo Lq.
 //
 // Transposed scores.  Each wavefront computes S^T = K * Q^T with K as the MFMA A operand
 // (32 keys x 16 dims) and Q^T as the B operand (16 dims x 32 queries, register resident
 // for the whole key loop).  The 32x32 fp32 result then holds one query per lane column:
 // lane l owns query l%32 and 16 of the 32 keys, the other 16 sitting in lane l^32.  Row
 // max = an in-lane max plus one cross-half exchange (needed for the first tile only: its
-// maximum is the reference for the whole sweep); the row sum stays per-lane until the end.  Those same registers, rounded to 16 bits, are directly the B operand of
+// maximum is the reference for the whole sweep); the row sum stays per-lane until the end.
+// Those same registers, rounded to 16 bits, are directly the B operand of
 // O^T += V^T * P^T (k index = key): no trip through LDS for P.  The key order inside the
 // B operand is fixed by the accumulator layout, so V^T must be read in that same
 // key order, which the transposing LDS reads of V provide.  O^T lives in 32x32 accumulators
@@ -27,8 +31,8 @@
 // Pipeline.  K and V tiles of 32 keys are copied straight from HBM into LDS (no register
 // staging) into rings of four stages.  Iteration t of the key loop reads K of tile t (S^T)
 // and V of tile t-1 (the P.V product of the previous tile, under which the softmax of tile
-// t runs); tile t+1 is landing, and tile t+2 is copied after the one workgroup barrier of
-// the iteration, one wave per step.  Each wavefront owns 64 query rows (two 32-row MFMA
+// t runs, one slice after each MFMA); tile t+1 is landing, and tile t+2 is copied after
+// the one workgroup barrier of the iteration, one wave per step.  Each wavefront owns 64 query rows (two 32-row MFMA
 // blocks), so every K and V fragment read from LDS feeds two MFMAs; Q stays in registers
 // and the output accumulator in AGPRs for the whole key loop.
 #include <hip/hip_runtime.h>
@@ -261,7 +265,9 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
   // causal: the last query tiles see the most keys; dispatching them first keeps the
   // light tiles for the end of the grid
   if (p.causal) qtile = p.n_qtiles - 1 - qtile;
-  const int bh = __builtin_amdgcn_readfirstlane(tile_id / p.n_qtiles);  // b*Hq + hq
+  // (row blocks as the host passes them: with each key/value group as one block, p.Hq =
+  // Hkv and p.G = 1)
+  const int bh = __builtin_amdgcn_readfirstlane(tile_id / p.n_qtiles);  // b*p.Hq + hq
   const int hq = __builtin_amdgcn_readfirstlane(bh % p.Hq);
   const int b = __builtin_amdgcn_readfirstlane(bh / p.Hq);
   const int hkv = __builtin_amdgcn_readfirstlane(hq / p.G);

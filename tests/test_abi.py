@@ -257,3 +257,42 @@ def test_plan_ex_names_the_causal_kernel():
     with pytest.raises(fa.AttnError) as e:
         fa.attn_plan_ex(1, 8, 2, 512, 512, 128, fa.ATTN_BF16, 8)
     assert e.value.code == -10
+
+
+def fwd_ex(nsplit, ws, ws_bytes, flags=0, **over):
+    a = dict(GOOD)
+    a.update(over)
+    return fa.attn_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Lq"], a["Lk"], a["D"], a["scale"], a["in_dtype"], flags, nsplit, ws,
+                          ws_bytes, None)
+
+
+WS = 15 * GB  # a fake, 256-byte aligned workspace address clear of the other arguments
+
+
+def test_fwd_ex_rejects_bad_workspace_before_any_launch():
+    need = fa.attn_workspace_bytes(GOOD["B"], GOOD["Hq"], GOOD["Lq"], GOOD["D"], 4)
+    assert need > 0
+    assert fwd_ex(4, None, 0) == -12                 # missing
+    assert fwd_ex(4, WS, need - 1) == -12            # too small
+    assert fwd_ex(4, WS + 16, need) == -12           # not 256-byte aligned
+    assert fwd_ex(4, Q, need) == -12                 # overlaps q
+    assert fwd_ex(4, O - need + 256, need) == -12    # overlaps o
+    # argument errors come first, whatever the workspace
+    assert fwd_ex(4, None, 0, flags=8) == -10
+    assert fwd_ex(300, WS, need) == -11
+    assert fwd_ex(4, WS, need, D=64) == -3
+
+
+def test_merge_and_partial_reject_before_any_launch():
+    assert fa.attn_merge(P_O, P_L, 0, 10, 128, O, L, fa.ATTN_F16, None) == -11
+    assert fa.attn_merge(P_O, P_L, 2, 10, 100, O, L, fa.ATTN_F16, None) == -3
+    assert fa.attn_merge(P_O, None, 2, 10, 128, O, L, fa.ATTN_F16, None) == -1
+    assert fa.attn_merge(P_O, P_L, 2, 10, 128, P_O, L, fa.ATTN_F16, None) == -8
+    a = GOOD
+    assert fa.attn_fwd_partial(a["q"], a["k"], a["v"], P_O, None, a["B"], a["Hq"], a["Hkv"],
+                               a["Lq"], a["Lk"], a["D"], a["scale"], a["in_dtype"], 0, 2,
+                               None) == -1
+    assert fa.attn_fwd_partial(a["q"], a["k"], a["v"], P_O, P_L, a["B"], a["Hq"], a["Hkv"],
+                               a["Lq"], a["Lk"], a["D"], a["scale"], a["in_dtype"], 0, 0,
+                               None) == -11
