@@ -100,6 +100,13 @@ struct Params {
   }                                                                                       \
   static __device__ __forceinline__ void mfma_v(u32x4 a, u32x4 b, f32x16& c) {            \
     asm volatile(OPC " %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));                        \
+  }                                                                                       \
+  /* the same with the B operand held in AGPRs */                                         \
+  static __device__ __forceinline__ void mfma_va0(u32x4 a, u32x4 b, f32x16& c) {          \
+    asm volatile(OPC " %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));                        \
+  }                                                                                       \
+  static __device__ __forceinline__ void mfma_va(u32x4 a, u32x4 b, f32x16& c) {           \
+    asm volatile(OPC " %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));                        \
   }
 
 template <typename T>
@@ -141,9 +148,12 @@ struct Elt<__bf16> {
   }
 };
 
-// Wait states between the last MFMA writing x or y and any other use of them (see above).
-__device__ __forceinline__ void mfma_fence_v(f32x16& x, f32x16& y) {
-  asm volatile("s_nop 11" : "+v"(x), "+v"(y));
+// Wait states between the last MFMA writing the score accumulators and any other use of
+// them (see above).
+template <int N>
+__device__ __forceinline__ void mfma_fence_v(f32x16 (&x)[N]) {
+  if constexpr (N == 1) asm volatile("s_nop 11" : "+v"(x[0]));
+  else asm volatile("s_nop 11" : "+v"(x[0]), "+v"(x[1]));
 }
 
 // Materialise x here: the compiler may not sink its computation past this point (the
@@ -219,20 +229,25 @@ __device__ __forceinline__ void lds_dma16_so(i32x4 rsrc, uint32_t voffset, uint3
 constexpr float kGrowth = 32768.0f;
 
 template <int D, typename T, bool NEG>
-__global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Params p) {
   constexpr int QB = attn_cfg::Tile<D>::QB;
   constexpr int BN = attn_cfg::Tile<D>::BN;
   constexpr int NSTAGE = attn_cfg::Tile<D>::STAGES;
-  static_assert(BN == 32 && QB == 2, "two 32-row query blocks, one 32-key block per tile");
+  static_assert(BN == 32 && (QB == 1 || QB == 2), "one or two 32-row query blocks per wave, "
+                "one 32-key block per tile");
+  constexpr int THREADS = attn_cfg::threads<D>();
+  constexpr int WAVES = attn_cfg::Tile<D>::WAVES;
   static_assert(NSTAGE == 4, "tiles t-1 (V), t (K), t+1, t+2 (in flight) resident");
   constexpr int KS = D / 16;    // contraction steps of S^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int TILE = BN * D;  // elements of one K (or V) tile
-  constexpr int LOADS = BN * CPR / attn_cfg::kThreads;     // 16-byte copies per thread per tile
-  constexpr int ROWS_PER_LOAD = attn_cfg::kThreads / CPR;  // tile rows one copy round covers
-  constexpr int BM = attn_cfg::block_m(QB);
-  constexpr int NSTEP = 2 * DB;  // P.V steps per tile, two MFMAs (one per query block) each
+  constexpr int LOADS = BN * CPR / THREADS;     // 16-byte copies per thread per tile
+  constexpr int ROWS_PER_LOAD = THREADS / CPR;  // tile rows one copy round covers
+  static_assert(LOADS >= 1 && BN * CPR % THREADS == 0, "whole copy rounds per tile");
+  constexpr int BM = attn_cfg::block_m<D>();
+  constexpr int NSTEP = 2 * DB;  // P.V steps per tile, QB MFMAs (one per query block) each
+  constexpr int NELEM = 16 * QB;  // scores per lane per tile
   constexpr int VPRE = 2;        // S^T steps before the end at which the first V reads issue
   // NEG: scale < 0, so the largest scaled score comes from the smallest raw score.
   constexpr float kWorst = NEG ? __builtin_inff() : -__builtin_inff();
@@ -362,7 +377,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       // copy uses the lane's fixed offset (no vector arithmetic, no reuse of one register).
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const uint32_t slot0 = (i * attn_cfg::kThreads + wave * 64) * 16;  // wave-uniform
+        const uint32_t slot0 = (i * THREADS + wave * 64) * 16;  // wave-uniform
         const uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
         lds_dma16_so(rk, vk[i & 1], rows, ks + slot0);
         lds_dma16_so(rv, vv, rows, vs + slot0);
@@ -372,7 +387,7 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       // so the row offset goes into the range-checked per-lane offset.
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const uint32_t slot0 = (i * attn_cfg::kThreads + wave * 64) * 16;
+        const uint32_t slot0 = (i * THREADS + wave * 64) * 16;
         // (rows laundered: added here, not hoisted into loop-invariant registers)
         uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
         asm volatile("" : "+s"(rows));
@@ -382,6 +397,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
     }
   };
 
+  // With two wavefronts per SIMD (HD=128) a wavefront has 256 registers, which the compiler
+  // splits evenly between VGPRs and AGPRs once AGPRs are in use; the Q^T fragments, read
+  // only by the S^T MFMAs, then live in AGPRs next to the output accumulator.
+  constexpr bool Q_AGPR = WAVES > 4;
   // Q^T operand fragments, register resident for the whole key loop: lane l holds query
   // row l%32 of block qb, dims 16*kk + 8*(l/32) .. +7.  Rows past Lq re-read row Lq-1
   // (never stored).
@@ -450,8 +469,13 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       if (kk == KS - VPRE) tail_loads();  // first V fragments of the P.V steps
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if (kk == 0) Elt<T>::mfma_v0(kf[kk % 3], qf[qb][kk], sacc[qb]);
-        else Elt<T>::mfma_v(kf[kk % 3], qf[qb][kk], sacc[qb]);
+        if constexpr (Q_AGPR) {
+          if (kk == 0) Elt<T>::mfma_va0(kf[kk % 3], qf[qb][kk], sacc[qb]);
+          else Elt<T>::mfma_va(kf[kk % 3], qf[qb][kk], sacc[qb]);
+        } else {
+          if (kk == 0) Elt<T>::mfma_v0(kf[kk % 3], qf[qb][kk], sacc[qb]);
+          else Elt<T>::mfma_v(kf[kk % 3], qf[qb][kk], sacc[qb]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -587,7 +611,11 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
 
   // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
   // (PV) with the softmax of tile t in slices underneath.
-  constexpr int SYNC_STEP = NSTEP - 4;  // three P.V steps remain after the sync point
+  // P.V step of the synchronisation point: four steps before the end, so that the copies
+  // issued after it have most of an iteration to land; the waves issue them in turn,
+  // WAVES/4 per step.
+  constexpr int SYNC_STEP = NSTEP - 4;
+  constexpr int COPY_WAVES = WAVES / 4;  // waves issuing copies per step
   u32x4 kf[3];
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
   auto iteration = [&](auto pv_tag, auto st_tag, int t, u32x4 (&pprev)[QB][2],
@@ -602,17 +630,17 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
         vf[1] = vfrag_load(VST, 1);
       }
     });
-    // Each P.V step is two half-steps: one MFMA (query block qb), then a slice of VALU or
+    // Each P.V step is QB sub-steps: one MFMA (query block qb), then a slice of VALU or
     // copy work that issues while that MFMA runs.  A wave issues in order, so work placed
-    // after an MFMA overlaps it only until the next MFMA: one half-step per MFMA gives
+    // after an MFMA overlaps it only until the next MFMA: one sub-step per MFMA gives
     // every MFMA its own window.  Exponentials (quarter-rate) are spread one or two per
-    // window over all half-steps after the first.
+    // window over all sub-steps after the first (tile 0: after its row maxima).
     // (the wave index laundered per iteration: the compiler would otherwise keep one
     // loop-invariant lane mask per copy step, and spill them)
     int wv = wave;
     asm volatile("" : "+s"(wv));
-    constexpr int H = 2 * NSTEP;                  // half-steps
-    constexpr int EXP0 = PV ? 1 : 3;              // first half-step with exponentials
+    constexpr int H = QB * NSTEP;                 // sub-steps
+    constexpr int EXP0 = PV ? 1 : QB + 1;         // first sub-step with exponentials
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if constexpr (PV) {
@@ -620,26 +648,27 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       }
 #pragma unroll
       for (int hb = 0; hb < QB; ++hb) {
-        const int h = 2 * s + hb;
+        const int h = QB * s + hb;
         if constexpr (PV) Elt<T>::acc_mfma(hb * DB + (s >> 1), vf[s % 3], pprev[hb][s & 1]);
         __builtin_amdgcn_sched_barrier(0);
         if (h == 0) {
-          mfma_fence_v(sacc[0], sacc[1]);
+          mfma_fence_v(sacc);
           mask_keys(sacc, t);
-          if (!PV) row_max(sacc, 0);  // tile 0 only: it fixes the reference
-        } else if (!PV && h == 1) {
-          row_max(sacc, 1);
-        } else if (!PV && h == 2) {
+        }
+        // tile 0 only: its row maxima fix the reference
+        if (!PV && h < QB) row_max(sacc, h);
+        if (!PV && h == QB) {
           set_reference();
           finite_reference();
         }
         if (h >= EXP0)
-          exp_slice(sacc, pcur, 32 * (h - EXP0) / (H - EXP0), 32 * (h - EXP0 + 1) / (H - EXP0));
-        if (h == 2 * SYNC_STEP) sync_point(t);
-        // copies of tile t+2, one wave per step after the synchronisation point, so that
-        // the four waves' copies do not queue up behind each other
-        static_assert(SYNC_STEP + attn_cfg::kWaves == NSTEP, "one copy step per wave");
-        if (hb == QB - 1 && s >= SYNC_STEP && t + 2 < ntiles && wv == s - SYNC_STEP)
+          exp_slice(sacc, pcur, NELEM * (h - EXP0) / (H - EXP0),
+                    NELEM * (h - EXP0 + 1) / (H - EXP0));
+        if (h == QB * SYNC_STEP) sync_point(t);
+        // copies of tile t+2 in the steps from the synchronisation point on, a few waves
+        // per step, so that the waves' copies do not queue up behind each other
+        static_assert(WAVES % 4 == 0, "waves share the four copy steps evenly");
+        if (hb == QB - 1 && s >= SYNC_STEP && t + 2 < ntiles && wv / COPY_WAVES == s - SYNC_STEP)
           issue_tile(t + 2, (ST + 2) % NSTAGE);
         if (h == H - 1) {
 #pragma unroll
@@ -687,10 +716,10 @@ __global__ __launch_bounds__(attn_cfg::kThreads, 1) void attn_fwd_kernel(Params 
       kf[1] = kfrag(kstage(t % NSTAGE), 1);
       f32x16 sacc[QB];
       qk(kstage(t % NSTAGE), sacc, kf, [] {});
-      mfma_fence_v(sacc[0], sacc[1]);
+      mfma_fence_v(sacc);
       mask_keys(sacc, t);
-      row_max(sacc, 0);
-      row_max(sacc, 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) row_max(sacc, qb);
       set_reference();
     }
     finite_reference();
@@ -825,7 +854,7 @@ int launch(const Params& prm, int64_t grid, hipStream_t stream) {
   Params local = prm;
   void* args[] = {&local};
   const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)),
-                                       dim3(attn_cfg::kThreads), args, lds, stream);
+                                       dim3(attn_cfg::threads<D>()), args, lds, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 

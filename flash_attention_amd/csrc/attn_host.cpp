@@ -21,7 +21,7 @@ bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
 }
 
 struct PlanInternal {
-  int qb, bn, stages, block_m, lds;
+  int waves, qb, bn, stages, block_m, lds;
 };
 
 bool plan_for_d(int64_t D, PlanInternal* p);
@@ -37,17 +37,20 @@ int64_t query_tiles(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D) {
 bool plan_for_d(int64_t D, PlanInternal* p) {
   using namespace attn_cfg;
   if (D == 128) {
+    p->waves = Tile<128>::WAVES;
     p->qb = Tile<128>::QB;
     p->bn = Tile<128>::BN;
     p->stages = Tile<128>::STAGES;
+    p->block_m = block_m<128>();
   } else if (D == 256) {
+    p->waves = Tile<256>::WAVES;
     p->qb = Tile<256>::QB;
     p->bn = Tile<256>::BN;
     p->stages = Tile<256>::STAGES;
+    p->block_m = block_m<256>();
   } else {
     return false;
   }
-  p->block_m = block_m(p->qb);
   p->lds = lds_bytes(static_cast<int>(D), p->bn, p->stages);
   return true;
 }
@@ -130,7 +133,7 @@ int fill_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_
   plan_for_d(D, &p);
   plan->block_m = p.block_m;
   plan->block_n = p.bn;
-  plan->waves = attn_cfg::kWaves;
+  plan->waves = p.waves;
   plan->lds_bytes = p.lds;
   plan->grid = query_tiles(Hq, Hkv, Lq, D) * B * nsplit;
   std::memset(plan->kernel, 0, sizeof plan->kernel);
