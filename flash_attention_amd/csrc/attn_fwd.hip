@@ -37,6 +37,7 @@
 // and the output accumulator in AGPRs for the whole key loop.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -845,12 +846,21 @@ int launch(const Params& prm, int64_t grid, hipStream_t stream) {
   static_assert(lds <= 160 * 1024, "LDS budget of one CU exceeded");
   const void* fn = prm.c < 0.f ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, true>)
                                : reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, false>);
-  static const hipError_t attr[2] = {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, false>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds),
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, true>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds)};
-  (void)attr;
+  // The LDS size above the default limit is a per-device attribute of the kernel: set it
+  // the first time a device launches this instantiation (one bit per device; a device past
+  // the 64th sets it on every launch).
+  static std::atomic<uint64_t> lds_ready{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_E_LAUNCH;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit == 0 || (lds_ready.load(std::memory_order_acquire) & bit) == 0) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return ATTN_E_LAUNCH;
+    lds_ready.fetch_or(bit, std::memory_order_release);
+  }
   Params local = prm;
   void* args[] = {&local};
   const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)),

@@ -177,7 +177,8 @@ int attn_validate_ex(const void* q, const void* k, const void* v, const void* o,
   if (nsplit < 0 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
   const int rc = attn_validate(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype);
   if (rc != ATTN_OK) return rc;
-  return check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, nsplit > 0 ? nsplit : ATTN_MAX_SPLITS);
+  // (nsplit = 0: the planner lowers its choice until the grid fits)
+  return check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, nsplit > 0 ? nsplit : 1);
 }
 
 int attn_validate_partial(const void* q, const void* k, const void* v, const float* o_part,

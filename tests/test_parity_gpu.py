@@ -250,3 +250,16 @@ def test_reference_growth_last_tile_and_repeated():
     q, k, v = _growing_scores(D, "f16", 900, [(100, 150.0), (300, 300.0), (500, 450.0),
                                               (899, 600.0)], seed=23)
     parity(q, k, v, scale_of(D), "f16", what="growth repeated")
+
+
+@pytest.mark.parametrize("D,dt", [(128, "f16"), (128, "bf16"), (256, "f16")])
+@pytest.mark.parametrize("causal,nsplit", [(False, 3), (True, 1), (True, 2)])
+def test_reference_growth_with_mask_and_splits(D, dt, causal, nsplit):
+    """Scores outgrowing the first tile's maximum, in several tiles (a restart of the key
+    sweep), under the causal mask and inside key splits (each split has its own first tile
+    and its own restart)."""
+    _announce("growth D=%d %s causal=%s nsplit=%d" % (D, dt, causal, nsplit))
+    q, k, v = _growing_scores(D, dt, 900, [(130, 200.0), (480, 350.0), (899, 500.0)],
+                              seed=24 + nsplit)
+    parity(q, k, v, scale_of(D), dt, what="growth causal=%s nsplit=%d" % (causal, nsplit),
+           causal=causal, nsplit=nsplit)
