@@ -805,7 +805,7 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
     const int row = qrow0 + qb * 32 + (lane_e & 31);
     const size_t orow = (size_t)bh * p.Lq + min(row, p.Lq - 1);
     const size_t prow = (size_t)split * p.part_rows + orow;
-    uint16_t* dst = p.o + orow * D + 4 * (lane_e >> 5);
+    uint16_t* dst16 = p.o + orow * D + 8 * (lane_e >> 5);  // 16-byte stores (see below)
     float* pdst = p.o_part + prow * D + 4 * (lane_e >> 5);
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -822,11 +822,24 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
                 make_float4(x[4 * g] * inv, x[4 * g + 1] * inv, x[4 * g + 2] * inv,
                             x[4 * g + 3] * inv);
         } else {
+          // Chunk g of this lane holds dims 8g + 4hi .. +3 of the 32-dim block; the lane
+          // l^32 holds the other four dims of each group of eight.  Exchanging one chunk of
+          // two per pair lets each lane store 16 contiguous bytes: lane hi = 0 dims 0-7 and
+          // 16-23, lane hi = 1 dims 8-15 and 24-31.
+          u32x2 w[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x2 w = {Elt<T>::pack2(x[4 * g] * inv, x[4 * g + 1] * inv),
-                             Elt<T>::pack2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
-            *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * g) = w;
+          for (int g = 0; g < 4; ++g)
+            w[g] = (u32x2){Elt<T>::pack2(x[4 * g] * inv, x[4 * g + 1] * inv),
+                           Elt<T>::pack2(x[4 * g + 2] * inv, x[4 * g + 3] * inv)};
+          const int h = lane_e >> 5;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const u32x2 send = h ? w[2 * j] : w[2 * j + 1];
+            const u32x2 recv = {static_cast<uint32_t>(__shfl_xor(static_cast<int>(send[0]), 32)),
+                                static_cast<uint32_t>(__shfl_xor(static_cast<int>(send[1]), 32))};
+            const u32x2 lo = h ? recv : w[2 * j];
+            const u32x2 up = h ? w[2 * j + 1] : recv;
+            *reinterpret_cast<u32x4*>(dst16 + db * 32 + 16 * j) = (u32x4){lo[0], lo[1], up[0], up[1]};
           }
         }
       }
