@@ -332,7 +332,7 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
 
   // ---- direct HBM->LDS copies of K and V tiles ----
   // Copy round i of this thread moves tile row r = i*ROWS_PER_LOAD + r0, 16-byte chunk c0
-  // (r0, c0 fixed per lane), into LDS slot i*256 + tid.  The buffer starts at the tile and
+  // (r0, c0 fixed per lane), into LDS slot i*THREADS + tid.  The buffer starts at the tile and
   // holds the bytes left in K (V), so rows past Lk read as zeros (their scores are masked,
   // their weights zero).  The K swizzle depends on i only through its parity (when a round
   // covers 8 rows), the V swizzle not at all.
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
   // dim i of those 4 rows.  Lane block b16 = lane/16: half h = b16/2 selects keys 4h..4h+3
   // (of each group of 8), b16%2 selects dims 16..31 of the 32-dim block db.  The chunk of
   // those dims sits at slot (4db + 2*(b16%2) + c/2) ^ 4e: in bytes (64db) ^ v0, v0 < 256.
-  // With the row start (a multiple of 512) and the 8-byte half (bit 3) that is
+  // With the row start (a multiple of 256) and the 8-byte half (bit 3) that is
   // vbase ^ (64*(db%4)) + 256*(db/4): the XOR touches bits 6-7 only.
   uint32_t vbase;
   {
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
   }
   const char* const smem_b = reinterpret_cast<const char*>(smem);
 
-  // Output accumulator O^T, block (qb, db) = AGPR block qb*DB + db (attn_agpr.h).
+  // Output accumulator O^T, block (qb, db) = AGPR block qb*DB + db (pinned, attn_agpr.h).
   float m[QB], l[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
   auto kfrag = [&](const char* ks, int kk) {
     return *reinterpret_cast<const u32x4*>(ks + krow + ((32u * kk) ^ k0));
   };
-  // S^T(t) = K(t) Q^T, fp32 accumulation, both query blocks sharing each K fragment.  The
+  // S^T(t) = K(t) Q^T, fp32 accumulation, the QB query blocks sharing each K fragment.  The
   // first two fragments arrive prefetched in kf[0..1]; the rest are fetched two steps ahead,
   // and the scheduling barriers keep the compiler from hoisting all of them (64 registers).
   auto qk = [&](const char* ks, f32x16 (&sacc)[QB], u32x4 (&kf)[3], auto&& tail_loads) {
