@@ -177,3 +177,36 @@ def test_merge_without_lse_and_single_part():
     o, lse = fa.merge(o_part.to(dev), lse_part.to(dev), lse=False)
     torch.cuda.synchronize()
     assert lse is None and torch.equal(o.cpu(), o_part[0])
+
+
+def _random_cases(n=48, seed=20261202):
+    """Seeded random mixes of every option: shapes with ragged tails, GQA ratios, both
+    head dims and dtypes, causal or not, split counts (0 = the planner's), scale sign."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        lq = int(rng.integers(1, 700))
+        lk = int(rng.integers(1, 2500))
+        d = int(rng.choice([128, 256]))
+        dt = str(rng.choice(["f16", "bf16"]))
+        causal = bool(rng.integers(0, 2))
+        nsplit = int(rng.choice([1, 1, 2, 3, 7, 0]))
+        sgn = -1.0 if rng.random() < 0.15 else 1.0
+        cases.append((int(rng.integers(1, 3)), hkv * g, hkv, lq, lk, d, dt, causal, nsplit, sgn,
+                      13000 + i))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=["r%d_B%d_H%d_%d_L%dx%d_D%d_%s_c%d_ns%d_%+d" % (
+    i, *c[:8], c[8], int(c[9])) for i, c in enumerate(RANDOM)])
+def test_random_options(case):
+    B, Hq, Hkv, Lq, Lk, D, dt, causal, nsplit, sgn, seed = case
+    _announce("random " + str(case))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, dt, seed=seed)
+    parity(q, k, v, sgn * scale_of(D), dt, what="random " + str(case), causal=causal,
+           nsplit=nsplit)
