@@ -190,6 +190,23 @@ def main():
     print("[bench] kernel ms (events, mean over %d launches) %.4f; wall/step %.4f ms" %
           (args.steps, kern_avg, ms_per_step), file=sys.stderr, flush=True)
 
+    # Per-launch distribution, outside the timed region: each launch between its own pair
+    # of events (the events' own packets sit between the kernels here).
+    per = []
+    for _ in range(min(args.steps, 20)):
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        step()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        per.append(a0.elapsed_time(a1))
+    per.sort()
+    try:
+        peak_rt, cus, khz = fa.attn_device_peak()
+    except fa.AttnError:
+        peak_rt, cus, khz = None, None, None
+
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.float16, device=dev)
@@ -220,6 +237,10 @@ def main():
                    "block_n": plan.block_n, "grid": plan.grid},
         "pct_of_peak": round(100 * value / PEAK_TFLOPS, 2),
         "kernel_ms_mean": round(kern_avg, 4),
+        "kernel_ms_median": round(per[len(per) // 2], 4),
+        "kernel_ms_min": round(per[0], 4),
+        "peak_runtime_tflops": round(peak_rt, 1) if peak_rt else None,
+        "device": {"compute_units": cus, "peak_clock_mhz": khz / 1000 if khz else None},
         "tflops_pages_formula": (round(flops_pages(w.Lq, w.Lk, w.D, w.Hq, w.B) /
                                        (ms_per_step * 1e-3) / 1e12, 2)
                                  if not w.causal else None),

@@ -91,6 +91,10 @@ def lib():
         L.attn_workspace_bytes.restype = _I64
         L.attn_plan_ex.argtypes = shape + [ctypes.c_int, U32, ctypes.POINTER(AttnPlan)]
         L.attn_plan_ex.restype = ctypes.c_int
+        L.attn_device_peak.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_int32)]
+        L.attn_device_peak.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -169,6 +173,15 @@ def attn_split_range(Lk, nsplit, s):
 
 def attn_workspace_bytes(B, Hq, Lq, D, nsplit):
     return lib().attn_workspace_bytes(B, Hq, Lq, D, nsplit)
+
+
+def attn_device_peak():
+    """(peak TFLOP/s, compute units, clock kHz) of the current device, or raise AttnError."""
+    t, cu, khz = ctypes.c_double(), ctypes.c_int32(), ctypes.c_int32()
+    rc = lib().attn_device_peak(ctypes.byref(t), ctypes.byref(cu), ctypes.byref(khz))
+    if rc != ATTN_OK:
+        raise AttnError(rc, attn_strerror(rc))
+    return t.value, cu.value, khz.value
 
 
 def attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags):

@@ -15,7 +15,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_merge.hip"),
-           os.path.join(CSRC, "attn_host.cpp")]
+           os.path.join(CSRC, "attn_device.hip"), os.path.join(CSRC, "attn_host.cpp")]
 
 # Packed fp32 VALU instructions are kept out of the device code: the compiler would
 # otherwise form them from ordinary float code.

@@ -227,6 +227,12 @@ int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int6
  * code for bad sizes.  Layout: O_part at offset 0, LSE_part at the next 256-byte boundary. */
 int64_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t nsplit);
 
+/* Dense fp16/bf16 MFMA peak of the current HIP device: compute units x peak shader clock x
+ * 4096 flop per clock per compute unit (the gfx950 rate of v_mfma_f32_32x32x16_{f16,bf16}).
+ * Any pointer may be NULL.  Returns ATTN_OK, or ATTN_E_LAUNCH if the HIP runtime reports no
+ * device. */
+int attn_device_peak(double* tflops, int32_t* compute_units, int32_t* clock_khz);
+
 /* Library version, "major.minor.patch". */
 const char* attn_version(void);
 
