@@ -111,6 +111,25 @@ def make_qkv(B, Hq, Hkv, Lq, Lk, D, dtype="f16", seed=0, dist="normal", k_mult=1
     return q.to(tdt), k.to(tdt), v.to(tdt)
 
 
+def make_qkv_on(device, B, Hq, Hkv, Lq, Lk, D, dtype="f16", seed=0):
+    """make_qkv's recipe (N(0,1) per element, seeds seed+1..seed+3, one rounding to 16 bits)
+    drawn by torch's generator of ``device`` (counter-based Philox on a GPU), so that inputs
+    of several GiB take seconds instead of minutes.  The values differ from make_qkv's for
+    the same seed; both are fixed by the seed.  The tensors stay on ``device``."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    out = []
+    for i, shape in enumerate(((B, Hq, Lq, D), (B, Hkv, Lk, D), (B, Hkv, Lk, D))):
+        g = torch.Generator(device=device).manual_seed(int(seed) + 1 + i)
+        t = torch.empty(shape, dtype=tdt, device=device)
+        flat = t.view(-1)
+        step = 1 << 28  # fp32 draws in slices of 1 GiB
+        for s in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - s)
+            flat[s:s + n] = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+        out.append(t)
+    return tuple(out)
+
+
 def workload_qkv(w: Workload):
     return make_qkv(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, w.dtype, seed=w.seed_base,
                     k_mult=w.k_mult)

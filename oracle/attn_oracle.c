@@ -171,7 +171,7 @@ static int run_rows(const double* q /* NULL: use q16 */, const uint16_t* q16, in
 #pragma omp atomic write
       oom = 1;
     } else {
-#pragma omp for schedule(dynamic, 4)
+#pragma omp for schedule(dynamic, 1)
       for (int64_t r = 0; r < nrows; ++r) {
         const int64_t flat = rows ? rows[r] : r;
         const int64_t i = flat % Lq;

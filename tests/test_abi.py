@@ -106,6 +106,20 @@ def test_validate_grid_limit():
     assert validate(Hq=256, Hkv=1, Lq=(1 << 31) // 256 // 256 + 1, Lk=64) == -2
 
 
+def test_validate_exact_length_limits():
+    # per-head offsets are 32-bit: Lk*D and (Hq/Hkv)*Lq*D up to 2^31 - 1 are accepted, one
+    # more row or key is refused (addresses far apart: the tensors span gigabytes here)
+    far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40)
+    for D in (128, 256):
+        lim = ((1 << 31) - 1) // D
+        assert validate(**far, D=D, Hq=2, Hkv=1, Lq=40, Lk=lim) == 0
+        assert validate(**far, D=D, Hq=2, Hkv=1, Lq=40, Lk=lim + 1) == -2
+        assert validate(**far, D=D, Hq=1, Hkv=1, Lq=lim, Lk=33) == 0
+        assert validate(**far, D=D, Hq=1, Hkv=1, Lq=lim + 1, Lk=33) == -2
+        assert validate(**far, D=D, Hq=16, Hkv=1, Lq=lim // 16, Lk=33) == 0
+        assert validate(**far, D=D, Hq=16, Hkv=1, Lq=lim // 16 + 1, Lk=33) == -2
+
+
 def test_lse_may_follow_o_directly():
     qbytes = 1 * 32 * 4096 * 256 * 2
     assert validate(lse=O + qbytes) == 0
