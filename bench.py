@@ -101,13 +101,54 @@ def compare_rows(o_gpu, lse_gpu, rows, o_ref, lse_ref):
             "lse_abs": float(np.abs(lg_f - lr_f).max()) if lg_f.size else 0.0}
 
 
+def sample_sclk(busy, seconds=1.5):
+    """Shader clock (MHz) under load: run busy() back to back for about `seconds` while
+    rocm-smi is polled; the median of the samples, or None without rocm-smi."""
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "--showclocks", "--csv"], capture_output=True,
+                                   text=True, timeout=20)
+            except (OSError, subprocess.SubprocessError):
+                return
+            lines = [x for x in r.stdout.splitlines() if "," in x]
+            if len(lines) >= 2:
+                head = lines[0].split(",")
+                if "sclk clock speed:" in head:
+                    cell = lines[1].split(",")[head.index("sclk clock speed:")]
+                    digits = "".join(ch for ch in cell if ch.isdigit())
+                    if digits:
+                        samples.append(int(digits))
+            stop.wait(0.2)
+
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    busy()  # the clock settles under load before the first sample
+    th.start()
+    while time.perf_counter() - t0 < seconds or (not samples and time.perf_counter() - t0 < 10):
+        busy()
+    stop.set()
+    th.join(timeout=25)
+    return sorted(samples)[len(samples) // 2] if samples else None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sampling window after the timed region")
     ap.add_argument("--cpu-rows", type=int, default=65536,
                     help="random query rows in the oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -193,7 +234,7 @@ def main():
     # Per-launch distribution, outside the timed region: each launch between its own pair
     # of events (the events' own packets sit between the kernels here).
     per = []
-    for _ in range(min(args.steps, 20)):
+    for _ in range(min(args.steps, 100)):
         a0 = torch.cuda.Event(enable_timing=True)
         a1 = torch.cuda.Event(enable_timing=True)
         a0.record(stream)
@@ -206,6 +247,14 @@ def main():
         peak_rt, cus, khz = fa.attn_device_peak()
     except fa.AttnError:
         peak_rt, cus, khz = None, None, None
+
+    sclk = None
+    if not args.no_clock:
+        def busy():
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+        sclk = sample_sclk(busy)
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 2
@@ -240,7 +289,11 @@ def main():
         "kernel_ms_median": round(per[len(per) // 2], 4),
         "kernel_ms_min": round(per[0], 4),
         "peak_runtime_tflops": round(peak_rt, 1) if peak_rt else None,
-        "device": {"compute_units": cus, "peak_clock_mhz": khz / 1000 if khz else None},
+        "device": {"compute_units": cus, "peak_clock_mhz": khz / 1000 if khz else None,
+                   "sclk_mhz_under_load": sclk},
+        # the same kernel time against the MFMA peak at the clock measured under this load
+        "frac_at_measured_clock": (round(achieved / (cus * sclk * 1e6 * 4096 / 1e12), 4)
+                                   if sclk and cus else None),
         "tflops_pages_formula": (round(flops_pages(w.Lq, w.Lk, w.D, w.Hq, w.B) /
                                        (ms_per_step * 1e-3) / 1e12, 2)
                                  if not w.causal else None),

@@ -163,6 +163,11 @@ static int run_rows(const double* q /* NULL: use q16 */, const uint16_t* q16, in
   (void)nthreads;
 #endif
   int oom = 0;
+  /* rows in runs of four (neighbouring rows share their key/value head in cache), one at a
+     time when there are too few rows to keep every thread busy that way */
+#ifdef _OPENMP
+  const int chunk = nrows >= 16 * (int64_t)omp_get_max_threads() ? 4 : 1;
+#endif
 #pragma omp parallel
   {
     double* e = (double*)malloc(sizeof(double) * (size_t)Lk);
@@ -171,7 +176,7 @@ static int run_rows(const double* q /* NULL: use q16 */, const uint16_t* q16, in
 #pragma omp atomic write
       oom = 1;
     } else {
-#pragma omp for schedule(dynamic, 1)
+#pragma omp for schedule(dynamic, chunk)
       for (int64_t r = 0; r < nrows; ++r) {
         const int64_t flat = rows ? rows[r] : r;
         const int64_t i = flat % Lq;
