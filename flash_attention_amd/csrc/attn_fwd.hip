@@ -949,6 +949,7 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int in_dtype, void* stream) {
   const int rc = attn_validate(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype);
   if (rc != ATTN_OK) return rc;
+  if (B * Hq * Lq == 0) return ATTN_OK;  // no query row: nothing to launch
   attn_plan_t plan;
   attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
   const Params prm = make_params(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D,
@@ -969,6 +970,7 @@ int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
   const int rc = attn_validate_partial(q, k, v, o_part, lse_part, B, Hq, Hkv, Lq, Lk, D, scale,
                                        in_dtype, flags, nsplit);
   if (rc != ATTN_OK) return rc;
+  if (B * Hq * Lq == 0) return ATTN_OK;
   attn_plan_t plan;
   attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
   const Params prm = make_params(q, k, v, nullptr, nullptr, o_part, lse_part, B, Hq, Hkv, Lq,
@@ -983,6 +985,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   int rc = attn_validate_ex(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, flags,
                             nsplit);
   if (rc != ATTN_OK) return rc;
+  if (B * Hq * Lq == 0) return ATTN_OK;  // (no workspace needed either)
   attn_plan_t plan;
   if (nsplit == 0) {
     attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, &plan);

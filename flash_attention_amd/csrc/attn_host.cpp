@@ -55,20 +55,23 @@ bool plan_for_d(int64_t D, PlanInternal* p) {
   return true;
 }
 
+// Sizes may be zero: B, Hq or Lq = 0 leaves no query row (nothing to do), Lk = 0 leaves
+// every row without keys (O = 0, LSE = -inf).  Hkv must be positive.
 int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                 int in_dtype, int64_t nsplit = 1) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return ATTN_E_SHAPE;
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Lq < 0 || Lk < 0 || D <= 0) return ATTN_E_SHAPE;
   if (D != 128 && D != 256) return ATTN_E_HEADDIM;
   if (Hq % Hkv != 0) return ATTN_E_GQA;
   if (in_dtype != ATTN_F16 && in_dtype != ATTN_BF16) return ATTN_E_DTYPE;
   const int64_t lim = (int64_t(1) << 31) - 1;
   if (Lq > lim / D || Lk > lim / D) return ATTN_E_SHAPE;  // per-head offsets fit in int32
-  if (B > lim || Hq > lim) return ATTN_E_SHAPE;
+  if (B > lim || Hq > lim || Hkv > lim) return ATTN_E_SHAPE;
+  if (B * Hkv > lim) return ATTN_E_SHAPE;  // (implied by the grid limit when Hq*Lq > 0)
   // the query heads of one key/value head run as one block of G*Lq rows: its row offsets
   // fit in int32 too
-  if (Hq / Hkv > lim / D / Lq) return ATTN_E_SHAPE;
+  if (Lq > 0 && Hq / Hkv > lim / D / Lq) return ATTN_E_SHAPE;
   const int64_t groups = query_tiles(Hq, Hkv, Lq, D);  // workgroups per (b, split)
-  if (groups > lim / B || groups * B > lim / nsplit) return ATTN_E_SHAPE;  // grid < 2^31
+  if (B > 0 && (groups > lim / B || groups * B > lim / nsplit)) return ATTN_E_SHAPE;  // < 2^31
   return ATTN_OK;
 }
 
@@ -106,6 +109,7 @@ double split_cost(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, in
 int64_t choose_nsplit(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                       int block_m) {
   int64_t best = 1;
+  if (B * Hq * Lq == 0 || Lk == 0) return best;  // no rows or no keys: nothing to spread
   double best_cost = split_cost(B, Hq, Hkv, Lq, Lk, D, 1, block_m);
   for (int64_t ns = 2; ns <= 128; ++ns) {
     if (split_len_of(Lk, ns) < 256) break;  // splits shorter than 8 tiles do not pay
@@ -151,16 +155,18 @@ extern "C" {
 int attn_validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                   float scale, int in_dtype) {
-  if (!q || !k || !v || !o) return ATTN_E_NULLPTR;
   int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype);
   if (rc != ATTN_OK) return rc;
+  const uint64_t qbytes = uint64_t(B) * Hq * Lq * D * 2;
+  const uint64_t kvbytes = uint64_t(B) * Hkv * Lk * D * 2;
+  const uint64_t lbytes = uint64_t(B) * Hq * Lq * 4;
+  // (a tensor of no elements may be NULL: it is never read or written)
+  if ((!q && qbytes) || (!k && kvbytes) || (!v && kvbytes) || (!o && qbytes))
+    return ATTN_E_NULLPTR;
   if (!std::isfinite(scale)) return ATTN_E_SCALE;
   auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
   if (mis16(q) || mis16(k) || mis16(v) || mis16(o)) return ATTN_E_ALIGN;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_E_ALIGN;
-  const uint64_t qbytes = uint64_t(B) * Hq * Lq * D * 2;
-  const uint64_t kvbytes = uint64_t(B) * Hkv * Lk * D * 2;
-  const uint64_t lbytes = uint64_t(B) * Hq * Lq * 4;
   if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) ||
       overlaps(o, qbytes, v, kvbytes))
     return ATTN_E_ALIAS;
@@ -185,19 +191,21 @@ int attn_validate_partial(const void* q, const void* k, const void* v, const flo
                           const float* lse_part, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
                           int64_t Lk, int64_t D, float scale, int in_dtype, uint32_t flags,
                           int64_t nsplit) {
-  if (!q || !k || !v || !o_part || !lse_part) return ATTN_E_NULLPTR;
   if (flags & ~ATTN_CAUSAL) return ATTN_E_FLAGS;
   if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
   int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, nsplit);
   if (rc != ATTN_OK) return rc;
-  if (!std::isfinite(scale)) return ATTN_E_SCALE;
-  auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
-  if (mis16(q) || mis16(k) || mis16(v) || mis16(o_part)) return ATTN_E_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0) return ATTN_E_ALIGN;
   const uint64_t qbytes = uint64_t(B) * Hq * Lq * D * 2;
   const uint64_t kvbytes = uint64_t(B) * Hkv * Lk * D * 2;
   const uint64_t pbytes = uint64_t(nsplit) * B * Hq * Lq * D * 4;
   const uint64_t lbytes = uint64_t(nsplit) * B * Hq * Lq * 4;
+  if ((!q && qbytes) || (!k && kvbytes) || (!v && kvbytes) || (!o_part && pbytes) ||
+      (!lse_part && lbytes))
+    return ATTN_E_NULLPTR;
+  if (!std::isfinite(scale)) return ATTN_E_SCALE;
+  auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (mis16(q) || mis16(k) || mis16(v) || mis16(o_part)) return ATTN_E_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0) return ATTN_E_ALIGN;
   const void* outs[2] = {o_part, lse_part};
   const uint64_t osz[2] = {pbytes, lbytes};
   for (int i = 0; i < 2; ++i)
@@ -211,9 +219,9 @@ int attn_validate_partial(const void* q, const void* k, const void* v, const flo
 int attn_validate_merge(const float* o_part, const float* lse_part, int64_t nsplit,
                         int64_t rows, int64_t D, const void* o, const float* lse,
                         int out_dtype) {
-  if (!o_part || !lse_part || !o) return ATTN_E_NULLPTR;
   if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
-  if (rows <= 0 || D <= 0) return ATTN_E_SHAPE;
+  if (rows < 0 || D <= 0) return ATTN_E_SHAPE;  // (rows = 0: nothing to merge)
+  if (rows > 0 && (!o_part || !lse_part || !o)) return ATTN_E_NULLPTR;
   if (D % 8 != 0 || D > 4096) return ATTN_E_HEADDIM;
   if (out_dtype != ATTN_F16 && out_dtype != ATTN_BF16 && out_dtype != ATTN_F32)
     return ATTN_E_DTYPE;
@@ -238,7 +246,7 @@ int attn_validate_merge(const float* o_part, const float* lse_part, int64_t nspl
 
 int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int64_t* end) {
   if (!begin || !end) return ATTN_E_NULLPTR;
-  if (Lk <= 0) return ATTN_E_SHAPE;
+  if (Lk < 0) return ATTN_E_SHAPE;
   if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS || s < 0 || s >= nsplit) return ATTN_E_SPLIT;
   if (nsplit == 1) {
     *begin = 0;
@@ -252,9 +260,13 @@ int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int6
 }
 
 int64_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t nsplit) {
-  if (B <= 0 || Hq <= 0 || Lq <= 0 || D <= 0) return ATTN_E_SHAPE;
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  if (B < 0 || Hq < 0 || Lq < 0 || D <= 0 || B > lim || Hq > lim || Lq > lim)
+    return ATTN_E_SHAPE;
   if (nsplit < 1 || nsplit > ATTN_MAX_SPLITS) return ATTN_E_SPLIT;
   if (nsplit == 1) return 0;
+  if (B * Hq > (int64_t(1) << 40) || (Lq > 0 && B * Hq > (int64_t(1) << 40) / Lq))
+    return ATTN_E_SHAPE;
   const int64_t rows = B * Hq * Lq;
   if (rows > (int64_t(1) << 40) / D / nsplit) return ATTN_E_SHAPE;
   return align256(nsplit * rows * D * 4) + align256(nsplit * rows * 4);
@@ -284,8 +296,8 @@ int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int
 const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "ok";
-    case ATTN_E_NULLPTR: return "q, k, v or o is a null pointer";
-    case ATTN_E_SHAPE: return "a size is non-positive or past the supported range";
+    case ATTN_E_NULLPTR: return "a tensor with elements is passed as a null pointer";
+    case ATTN_E_SHAPE: return "a size is negative, Hkv is not positive, or a size is past the supported range";
     case ATTN_E_HEADDIM: return "head dimension must be 128 or 256";
     case ATTN_E_GQA: return "Hq must be a multiple of Hkv";
     case ATTN_E_DTYPE: return "in_dtype must be ATTN_F16 or ATTN_BF16";
@@ -301,6 +313,6 @@ const char* attn_strerror(int code) {
   }
 }
 
-const char* attn_version(void) { return "0.2.0"; }
+const char* attn_version(void) { return "0.3.0"; }
 
 }  // extern "C"

@@ -106,6 +106,7 @@ extern "C" int attn_merge(const float* o_part, const float* lse_part, int64_t ns
                           void* stream) {
   const int rc = attn_validate_merge(o_part, lse_part, nsplit, rows, D, o, lse, out_dtype);
   if (rc != ATTN_OK) return rc;
+  if (rows == 0) return ATTN_OK;
   MergeParams p;
   p.o_part = o_part;
   p.lse_part = lse_part;

@@ -41,6 +41,12 @@
  * (context-parallel ring attention).  Splitting the keys gives short query
  * sequences enough workgroups to fill the GPU (split-K of section E.2).
  *
+ * Empty sizes.  B, Hq, Lq and Lk may be 0 (Hkv must be positive).  With no query row
+ * (B*Hq*Lq = 0) a call is valid, launches nothing and writes nothing.  With no key (Lk = 0)
+ * every row's softmax is over an empty set: its weighted sum is empty, O = 0, and its
+ * exponential sum is 0, LSE = ln 0 = -inf -- the values of a causal row that sees no key.
+ * A pointer to a tensor of no elements may be NULL.
+ *
  * Layouts.  All tensors are contiguous and row-major with the head dimension
  * fastest:  Q, O: [B, Hq, Lq, D];  K, V: [B, Hkv, Lk, D];  LSE: [B, Hq, Lq].
  * Partial results: O_part [nsplit, B, Hq, Lq, D] fp32, LSE_part
@@ -77,10 +83,11 @@ typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1, ATTN_F32 = 2 } attn_dtype_t;
 /* Return codes. */
 enum {
   ATTN_OK = 0,
-  ATTN_E_NULLPTR = -1, /* q, k, v or o is NULL (lse may be NULL: LSE is then not written) */
-  ATTN_E_SHAPE = -2,   /* B, Hq, Hkv, Lq or Lk <= 0, or a size past the supported range:
-                          Lq*D, (Hq/Hkv)*Lq*D and Lk*D must stay below 2^31, the grid
-                          below 2^31 blocks */
+  ATTN_E_NULLPTR = -1, /* q, k, v or o is NULL while that tensor has elements (lse may
+                          be NULL: LSE is then not written) */
+  ATTN_E_SHAPE = -2,   /* B, Hq, Lq or Lk < 0, Hkv <= 0, or a size past the supported
+                          range: Lq*D, (Hq/Hkv)*Lq*D and Lk*D must stay below 2^31,
+                          B*Hkv and the grid below 2^31 */
   ATTN_E_HEADDIM = -3, /* D is not 128 or 256 */
   ATTN_E_GQA = -4,     /* Hq is not a multiple of Hkv */
   ATTN_E_DTYPE = -5,   /* in_dtype is neither ATTN_F16 nor ATTN_BF16 */
@@ -204,6 +211,7 @@ int attn_validate_partial(const void* q, const void* k, const void* v, const flo
  *   o         [rows, D] output of element type out_dtype (ATTN_F16, ATTN_BF16, ATTN_F32),
  *             rounded to nearest even
  *   lse       [rows] fp32 output, or NULL
+ *   rows      0 or more (0: nothing to do, the pointers may be NULL)
  *   D         a positive multiple of 8, at most 4096
  * The inputs may come from attn_fwd_partial (rows = B*Hq*Lq) or from any source of
  * partial attention results with this layout, e.g. key shards held elsewhere.  o_part and
@@ -218,13 +226,14 @@ int attn_validate_merge(const float* o_part, const float* lse_part, int64_t nspl
                         int64_t rows, int64_t D, const void* o, const float* lse,
                         int out_dtype);
 
-/* Key range [*begin, *end) of split s (0 <= s < nsplit) of Lk keys: ranges of
+/* Key range [*begin, *end) of split s (0 <= s < nsplit) of Lk >= 0 keys: ranges of
  * ceil(ceil(Lk / nsplit) / 64) * 64 keys from key 0, the last ones cut at Lk or empty
  * (begin = end = Lk).  Pure CPU.  Returns ATTN_OK, ATTN_E_SHAPE or ATTN_E_SPLIT. */
 int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int64_t* end);
 
-/* Workspace bytes attn_fwd_ex needs for nsplit splits (0 for nsplit = 1), or a negative
- * code for bad sizes.  Layout: O_part at offset 0, LSE_part at the next 256-byte boundary. */
+/* Workspace bytes attn_fwd_ex needs for nsplit splits (0 for nsplit = 1 or no query row),
+ * or a negative code for bad sizes.  Layout: O_part at offset 0, LSE_part at the next
+ * 256-byte boundary. */
 int64_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t nsplit);
 
 /* Dense fp16/bf16 MFMA peak of the current HIP device: compute units x peak shader clock x

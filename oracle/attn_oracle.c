@@ -137,7 +137,9 @@ static int64_t visible_keys(int64_t i, int64_t Lq, int64_t Lk, int causal, int64
 
 static int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                        int causal, int64_t key_begin, int64_t lk_total) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lq <= 0 || Lk <= 0 || D <= 0) return -2;
+  /* Zero batches, heads or query rows: no row to compute.  Zero keys: every row sees
+     none (O = 0, LSE = -inf, as for a causal row before the first key). */
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Lq < 0 || Lk < 0 || D <= 0) return -2;
   if (Hq % Hkv != 0) return -4;
   if (causal != 0 && causal != 1) return -11;
   if (key_begin < 0 || lk_total < key_begin + Lk) return -12;
@@ -170,7 +172,7 @@ static int run_rows(const double* q /* NULL: use q16 */, const uint16_t* q16, in
 #endif
 #pragma omp parallel
   {
-    double* e = (double*)malloc(sizeof(double) * (size_t)Lk);
+    double* e = (double*)malloc(sizeof(double) * (size_t)(Lk > 0 ? Lk : 1));
     double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
     if (!e || !qrow) {
 #pragma omp atomic write
@@ -228,8 +230,8 @@ int oracle_attn_rows_u16(const uint16_t* q, const uint16_t* k, const uint16_t* v
   if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -5;
   if (!rows && nrows != B * Hq * Lq) return -9;
   const size_t nkv = (size_t)(B * Hkv * Lk * D);
-  double* K = (double*)malloc(sizeof(double) * nkv);
-  double* V = (double*)malloc(sizeof(double) * nkv);
+  double* K = (double*)malloc(sizeof(double) * (nkv > 0 ? nkv : 1));
+  double* V = (double*)malloc(sizeof(double) * (nkv > 0 ? nkv : 1));
   if (!K || !V) {
     free(K);
     free(V);

@@ -444,6 +444,35 @@ def pin_merge_identities(orc):
     assert np.all(np.isfinite(om)) and np.allclose(lm, 800 + math.log(2), atol=1e-12)
 
 
+def pin_empty_sizes(orc):
+    """No keys (Lk = 0): every row's weighted sum and exponential sum are empty, so O = 0
+    and LSE = ln 0 = -inf, with or without the mask and for 16-bit inputs; an empty key
+    slice merged with the rest leaves the rest unchanged.  No query rows (B, Hq or Lq = 0):
+    results of shape (0, D) and (0,)."""
+    rng = _rng(37)
+    D = 8
+    q = _f64((2, 4, 3, D), rng)
+    k0 = np.zeros((2, 2, 0, D))
+    for causal in (False, True):
+        o, lse = _run(orc, q, k0, k0, 0.5, causal=causal)
+        assert o.shape == (2, 4, 3, D) and not o.any(), causal
+        assert np.all(lse == -np.inf), causal
+    q16 = torch.from_numpy(q).to(torch.float16)
+    k16 = torch.zeros((2, 2, 0, D), dtype=torch.float16)
+    o, lse = _run(orc, q16, k16, k16, 0.5)
+    assert not o.any() and np.all(lse == -np.inf)
+    qf, kf, vf = _f64((1, 2, 4, D), rng), _f64((1, 1, 6, D), rng), _f64((1, 1, 6, D), rng)
+    o_full, l_full = orc.attention(qf, kf, vf, 0.3)
+    o_e, l_e = orc.attention(qf, kf[:, :, 6:], vf[:, :, 6:], 0.3, key_begin=6, lk_total=6)
+    assert not o_e.any() and np.all(l_e == -np.inf)
+    om, lm = orc.merge([o_full, o_e], [l_full, l_e])
+    assert np.array_equal(om, o_full) and np.array_equal(lm, l_full)
+    for qs, ks in [((0, 4, 3, D), (0, 2, 5, D)), ((2, 0, 3, D), (2, 2, 5, D)),
+                   ((2, 4, 0, D), (2, 2, 5, D)), ((2, 4, 0, D), (2, 2, 0, D))]:
+        o, lse = orc.attention(np.zeros(qs), _f64(ks, rng), _f64(ks, rng), 0.5)
+        assert o.shape == (0, D) and lse.shape == (0,), (qs, ks)
+
+
 PINS = [
     pin_worked_example,
     pin_single_key,
@@ -468,4 +497,5 @@ PINS = [
     pin_key_slice_is_sliced_input,
     pin_merge_of_key_splits,
     pin_merge_identities,
+    pin_empty_sizes,
 ]

@@ -83,7 +83,8 @@ def test_validate_accepts_good_arguments():
 
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
-    (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(Lq=0), -2), (dict(Lk=-1), -2),
+    (dict(B=-1), -2), (dict(Hq=-1), -2), (dict(Hkv=0), -2), (dict(Hkv=-2), -2), (dict(Lq=-1), -2),
+    (dict(Lk=-1), -2), (dict(k=None), -1), (dict(v=None), -1),
     (dict(Lq=(1 << 31) // 256 + 1), -2), (dict(Lk=1 << 24), -2),
     (dict(D=64), -3), (dict(D=192), -3), (dict(D=512), -3),
     (dict(Hq=32, Hkv=3), -4), (dict(Hq=2, Hkv=4), -4),
@@ -118,6 +119,47 @@ def test_validate_exact_length_limits():
         assert validate(**far, D=D, Hq=1, Hkv=1, Lq=lim + 1, Lk=33) == -2
         assert validate(**far, D=D, Hq=16, Hkv=1, Lq=lim // 16, Lk=33) == 0
         assert validate(**far, D=D, Hq=16, Hkv=1, Lq=lim // 16 + 1, Lk=33) == -2
+
+
+def test_empty_sizes():
+    # No query rows (B, Hq or Lq = 0): nothing to compute.  No keys (Lk = 0): every row's
+    # softmax is over an empty set, O = 0 and LSE = -inf.  Both are valid calls.
+    assert validate(B=0) == 0 and validate(Hq=0) == 0 and validate(Lq=0) == 0
+    assert validate(Lk=0) == 0 and validate(Lk=0, Lq=0) == 0
+    # a tensor of no elements may be NULL; one with elements may not
+    assert validate(q=None, o=None, lse=None, Lq=0) == 0
+    assert validate(q=None, k=None, v=None, o=None, lse=None, B=0) == 0
+    assert validate(k=None, v=None, Lk=0) == 0
+    assert validate(q=None, Lk=0) == -1 and validate(o=None, Lk=0) == -1
+    assert validate(Hq=0, Hkv=0) == -2
+    assert fa.attn_plan(1, 32, 2, 0, 4096, 256, fa.ATTN_F16).grid == 0
+    assert fa.attn_plan(0, 32, 2, 64, 4096, 256, fa.ATTN_F16).grid == 0
+    assert fa.attn_plan_ex(1, 32, 2, 16, 0, 256, fa.ATTN_F16, fa.ATTN_CAUSAL).nsplit == 1
+    assert fa.attn_plan_ex(1, 32, 2, 0, 16384, 256, fa.ATTN_F16, 0).nsplit == 1
+    assert [fa.attn_split_range(0, 4, s) for s in range(4)] == [(0, 0)] * 4
+    assert fa.attn_split_range(0, 1, 0) == (0, 0)
+    assert validate_partial(Lq=0, o_part=None, lse_part=None) == 0
+    assert validate_partial(Lk=0, k=None, v=None) == 0
+    assert validate_partial(Lk=0, o_part=None) == -1
+
+
+def test_calls_without_query_rows_launch_nothing():
+    # with no query row the entry points return ATTN_OK before any HIP call, so this runs
+    # without a GPU (and with NULL tensors)
+    args = (None, None, None, None, None)
+    kv = (None, K, V, None, None)  # keys exist (never read here): their pointers are checked
+    assert fa.attn_fwd(*args, 0, 32, 2, 128, 128, 256, 0.0625, fa.ATTN_F16) == 0
+    assert fa.attn_fwd_stream(*kv, 1, 32, 2, 0, 128, 128, 0.1, fa.ATTN_BF16, None) == 0
+    assert fa.attn_fwd_stream(*args, 1, 32, 2, 0, 128, 128, 0.1, fa.ATTN_BF16, None) == -1
+    assert fa.attn_fwd_ex(*args, 1, 0, 2, 16, 0, 256, 0.1, fa.ATTN_F16, fa.ATTN_CAUSAL, 4,
+                          None, 0, None) == 0
+    assert fa.attn_fwd_ex(*kv, 1, 32, 2, 0, 4096, 256, 0.1, fa.ATTN_F16, 0, 0, None, 0,
+                          None) == 0
+    assert fa.attn_fwd_partial(*kv, 1, 32, 2, 0, 64, 128, 0.1, fa.ATTN_F16, 0, 3, None) == 0
+    assert fa.attn_merge(None, None, 5, 0, 256, None, None, fa.ATTN_F32, None) == 0
+    # the checks still run first
+    assert fa.attn_fwd(*args, 0, 32, 2, 128, 128, 64, 0.0625, fa.ATTN_F16) == -3
+    assert fa.attn_fwd(*args, -1, 32, 2, 128, 128, 256, 0.0625, fa.ATTN_F16) == -2
 
 
 def test_lse_may_follow_o_directly():
@@ -207,7 +249,9 @@ def test_validate_merge():
     assert validate_merge(o=None) == -1 and validate_merge(o_part=None) == -1
     assert validate_merge(lse_part=None) == -1
     assert validate_merge(nsplit=0) == -11 and validate_merge(nsplit=257) == -11
-    assert validate_merge(rows=0) == -2 and validate_merge(D=0) == -2
+    assert validate_merge(rows=-1) == -2 and validate_merge(D=0) == -2
+    # no rows: nothing to merge, the pointers may be NULL
+    assert validate_merge(rows=0, o_part=None, lse_part=None, o=None, lse=None) == 0
     assert validate_merge(D=12) == -3 and validate_merge(D=4104) == -3
     assert validate_merge(out_dtype=3) == -5 and validate_merge(out_dtype=-1) == -5
     assert validate_merge(o=O + 8) == -7 and validate_merge(lse=L + 1) == -7
@@ -230,7 +274,7 @@ def test_split_ranges_partition_the_keys(Lk, nsplit):
 
 
 def test_split_range_errors():
-    for args, code in [((0, 1, 0), -2), ((10, 0, 0), -11), ((10, 2, 2), -11), ((10, 2, -1), -11),
+    for args, code in [((-1, 1, 0), -2), ((10, 0, 0), -11), ((10, 2, 2), -11), ((10, 2, -1), -11),
                        ((10, 257, 0), -11)]:
         with pytest.raises(fa.AttnError) as e:
             fa.attn_split_range(*args)
@@ -244,7 +288,8 @@ def test_workspace_bytes():
     l_bytes = -(-(4 * rows * 4) // 256) * 256
     assert fa.attn_workspace_bytes(2, 32, 1000, 128, 4) == o_bytes + l_bytes
     assert fa.attn_workspace_bytes(1, 32, 1024, 256, 0) == -11
-    assert fa.attn_workspace_bytes(0, 32, 1024, 256, 2) == -2
+    assert fa.attn_workspace_bytes(-1, 32, 1024, 256, 2) == -2
+    assert fa.attn_workspace_bytes(0, 32, 1024, 256, 2) == 0  # no rows, no partials
 
 
 @pytest.mark.parametrize("shape,expect", [

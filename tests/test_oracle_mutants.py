@@ -42,6 +42,9 @@ MUTANTS = {
     "causal_slice_local": ("const int64_t n = i + (lk_total - Lq) - key_begin + 1;",
                            "const int64_t n = i + (Lk - Lq) + 1;"),
     "empty_row_lse_zero": ("    *lse = -INFINITY;\n    return;", "    *lse = 0.0;\n    return;"),
+    "empty_keys_refused": ("Lq < 0 || Lk < 0 || D <= 0) return -2;",
+                           "Lq < 0 || Lk <= 0 || D <= 0) return -2;"),
+    "empty_rows_refused": ("if (B < 0 || Hq < 0 ||", "if (B <= 0 || Hq <= 0 ||"),
     # merge
     "merge_no_max": ("sum += exp(lse_parts[g * nrows + r] - top);",
                      "sum += exp(lse_parts[g * nrows + r]); top = 0.0;"),
