@@ -101,43 +101,70 @@ def compare_rows(o_gpu, lse_gpu, rows, o_ref, lse_ref):
             "lse_abs": float(np.abs(lg_f - lr_f).max()) if lg_f.size else 0.0}
 
 
-def sample_sclk(busy, seconds=1.5):
-    """Shader clock (MHz) under load: run busy() back to back for about `seconds` while
-    rocm-smi is polled; the median of the samples, or None without rocm-smi."""
-    import shutil
+# Shader-clock poller, run as a separate process that is started before this process touches
+# the GPU: it calls rocm-smi itself (a program started from a process that has initialised
+# the GPU would inherit that state).  Protocol: "start" on stdin begins polling, "stop" (or
+# end of input) ends it; the median MHz of the samples (or "null") comes back on stdout.
+_SCLK_POLLER = r"""
+import json, shutil, subprocess, sys, threading
+exe = shutil.which("rocm-smi")
+if sys.stdin.readline().strip() != "start" or exe is None:
+    print("null", flush=True)
+    sys.exit(0)
+stop = threading.Event()
+threading.Thread(target=lambda: (sys.stdin.readline(), stop.set()), daemon=True).start()
+samples = []
+while not stop.is_set():
+    try:
+        r = subprocess.run([exe, "--showclocks", "--csv"], capture_output=True, text=True,
+                           timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        break
+    lines = [x for x in r.stdout.splitlines() if "," in x]
+    if len(lines) >= 2:
+        head = lines[0].split(",")
+        if "sclk clock speed:" in head:
+            cell = lines[1].split(",")[head.index("sclk clock speed:")]
+            digits = "".join(ch for ch in cell if ch.isdigit())
+            if digits:
+                samples.append(int(digits))
+    stop.wait(0.2)
+print(json.dumps(sorted(samples)[len(samples) // 2] if samples else None), flush=True)
+"""
+
+
+def start_sclk_poller():
+    """The poller process (see above), or None; call before any GPU work.  None under a
+    profiler, whose preloaded library has initialised the GPU before this program began."""
     import subprocess
-    import threading
-    exe = shutil.which("rocm-smi")
-    if exe is None:
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
         return None
-    samples, stop = [], threading.Event()
+    try:
+        return subprocess.Popen([sys.executable, "-c", _SCLK_POLLER], stdin=subprocess.PIPE,
+                                stdout=subprocess.PIPE, text=True)
+    except OSError:
+        return None
 
-    def poll():
-        while not stop.is_set():
-            try:
-                r = subprocess.run([exe, "--showclocks", "--csv"], capture_output=True,
-                                   text=True, timeout=20)
-            except (OSError, subprocess.SubprocessError):
-                return
-            lines = [x for x in r.stdout.splitlines() if "," in x]
-            if len(lines) >= 2:
-                head = lines[0].split(",")
-                if "sclk clock speed:" in head:
-                    cell = lines[1].split(",")[head.index("sclk clock speed:")]
-                    digits = "".join(ch for ch in cell if ch.isdigit())
-                    if digits:
-                        samples.append(int(digits))
-            stop.wait(0.2)
 
-    th = threading.Thread(target=poll, daemon=True)
-    t0 = time.perf_counter()
+def sample_sclk(poller, busy, seconds=1.5):
+    """Shader clock (MHz) under load: busy() runs back to back for about `seconds` while the
+    poller samples rocm-smi; None without a poller or samples."""
+    if poller is None:
+        return None
     busy()  # the clock settles under load before the first sample
-    th.start()
-    while time.perf_counter() - t0 < seconds or (not samples and time.perf_counter() - t0 < 10):
+    poller.stdin.write("start\n")
+    poller.stdin.flush()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
         busy()
-    stop.set()
-    th.join(timeout=25)
-    return sorted(samples)[len(samples) // 2] if samples else None
+    poller.stdin.write("stop\n")
+    poller.stdin.flush()
+    try:
+        out, _ = poller.communicate(timeout=30)
+        return json.loads(out.strip().splitlines()[-1])
+    except Exception:  # the poller failed: no clock figure
+        poller.kill()
+        return None
 
 
 def parse():
@@ -162,6 +189,7 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
+    poller = None if args.no_clock else start_sclk_poller()  # before any GPU work
     import numpy as np
     import torch
 
@@ -254,7 +282,7 @@ def main():
             for _ in range(10):
                 step()
             torch.cuda.synchronize()
-        sclk = sample_sclk(busy)
+        sclk = sample_sclk(poller, busy)
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib * (1 << 20) // 2

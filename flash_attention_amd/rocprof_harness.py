@@ -35,7 +35,7 @@ COPY_MIB = 1024
 
 def _bench_cmd(workload, steps, warmup, calib):
     cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", workload,
-           "--steps", str(steps), "--warmup", str(warmup), "--no-cpu"]
+           "--steps", str(steps), "--warmup", str(warmup), "--no-cpu", "--no-clock"]
     if calib:
         cmd += ["--copy-calib-mib", str(COPY_MIB)]
     return cmd

@@ -20,6 +20,7 @@ float64 O rows [n, D] and LSE [n].
 """
 import ctypes
 import os
+import sys
 
 import numpy as np
 
@@ -37,6 +38,12 @@ class Oracle:
 
     def __init__(self, path=LIB_PATH):
         if not os.path.exists(path):
+            # built on first use, but never from a process that already drives the GPU (the
+            # compiler would start from it): build the oracle before any GPU work instead
+            torch = sys.modules.get("torch")
+            if torch is not None and torch.cuda.is_initialized():
+                raise RuntimeError("%s is not built; run `python -m oracle.build` (or "
+                                   "__graft_entry__.build()) before using the GPU" % path)
             from . import build as _b
             _b.build(out=path, quiet=True)
         self.path = path
