@@ -348,9 +348,19 @@ def main():
                 else np.full(len(rows), w.Lk))
         cpu_flops = 4 * w.D * int(nvis.sum())
         cm = compare_rows(o.cpu(), lse.cpu(), rows, o_ref, lse_ref)
+        cpu_model = None
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        cpu_model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         out["cpu_baseline"] = {
             "value": round(cpu_flops / csec / 1e12, 6), "unit": "TFLOPS", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model,
+            "ms_per_row": round(csec * 1e3 / len(rows), 4),
             "sample": "%d query rows of this workload (seeded: %d random + first/last tiles "
                       "and end rows of every head), fp64, %.1f s; extrapolated full oracle "
                       "%.0f s" % (len(rows), min(args.cpu_rows, w.B * w.Hq * w.Lq), csec,
