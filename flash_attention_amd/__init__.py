@@ -214,12 +214,26 @@ def _check_qkv(q, k, v):
             raise ValueError("%s must be 4-D [B,H,L,D]" % name)
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     B, Hq, Lq, D = q.shape
     Bk, Hkv, Lk, Dk = k.shape
     if (Bk, Dk) != (B, D) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
                                                              tuple(v.shape)))
     return B, Hq, Hkv, Lq, Lk, D
+
+
+def _check_out(name, t, shape, dtype, device):
+    """A caller-provided output must match exactly what the kernel writes."""
+    if t.device != device:
+        raise ValueError("%s must be on %s, not %s" % (name, device, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, not %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
 
 
 def fwd(q, k, v, scale=None, out=None, lse=None, return_lse=True, stream=None, causal=False,
@@ -239,8 +253,14 @@ def fwd(q, k, v, scale=None, out=None, lse=None, return_lse=True, stream=None, c
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out("out", out, tuple(q.shape), q.dtype, q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out("lse", lse, (B, Hq, Lq), torch.float32, q.device)
+    if workspace is not None:
+        _check_out("workspace", workspace, tuple(workspace.shape), torch.uint8, q.device)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     flags = ATTN_CAUSAL if causal else 0
     lse_ptr = lse.data_ptr() if lse is not None else None

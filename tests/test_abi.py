@@ -162,6 +162,23 @@ def test_calls_without_query_rows_launch_nothing():
     assert fa.attn_fwd(*args, -1, 32, 2, 128, 128, 256, 0.0625, fa.ATTN_F16) == -2
 
 
+def test_binding_output_check():
+    # the check fa.fwd applies to caller-provided outputs (pure Python, CPU tensors here)
+    import torch
+    dev = torch.device("cpu")
+    ok = torch.empty(1, 2, 3, 8, dtype=torch.float16)
+    fa._check_out("out", ok, (1, 2, 3, 8), torch.float16, dev)
+    with pytest.raises(ValueError):
+        fa._check_out("out", ok, (1, 2, 4, 8), torch.float16, dev)
+    with pytest.raises(TypeError):
+        fa._check_out("out", ok, (1, 2, 3, 8), torch.bfloat16, dev)
+    with pytest.raises(ValueError):
+        fa._check_out("out", ok.transpose(2, 3).contiguous().transpose(2, 3), (1, 2, 3, 8),
+                      torch.float16, dev)
+    with pytest.raises(ValueError):
+        fa._check_out("out", ok, (1, 2, 3, 8), torch.float16, torch.device("cuda:0"))
+
+
 def test_lse_may_follow_o_directly():
     qbytes = 1 * 32 * 4096 * 256 * 2
     assert validate(lse=O + qbytes) == 0

@@ -205,6 +205,35 @@ def test_rejected_call_writes_nothing():
     assert torch.isnan(o.float()).all()
 
 
+def test_binding_rejects_mismatched_outputs():
+    # caller-provided outputs must match what the kernel writes; a mismatch is refused
+    # before anything is launched
+    _announce("binding output checks")
+    dev = torch.device("cuda:0")
+    q = torch.randn(1, 4, 64, 128, device=dev).half()
+    k = torch.randn(1, 2, 80, 128, device=dev).half()
+    big = torch.full((2, 4, 64, 128), float("nan"), dtype=torch.float16, device=dev)
+    bad = [dict(out=big),                                       # wrong shape
+           dict(out=big[:1].float()),                           # wrong dtype
+           dict(out=torch.empty(1, 4, 128, 64, dtype=torch.float16,
+                                device=dev).transpose(2, 3)),    # not contiguous
+           dict(lse=torch.empty(1, 4, 65, device=dev)),
+           dict(lse=torch.empty(1, 4, 64, device=dev, dtype=torch.float16)),
+           dict(workspace=torch.empty(1 << 20, device=dev), nsplit=2)]  # not bytes
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)):
+            fa.fwd(q, k, k, **kw)
+    with pytest.raises(ValueError):
+        fa.fwd(q, k.cpu(), k)
+    torch.cuda.synchronize()
+    assert torch.isnan(big.float()).all()
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 4, 64, device=dev)
+    fa.fwd(q, k, k, out=o, lse=lse)  # matching outputs are accepted
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
 def test_scale_sign_and_zero():
     """Negative and zero scales follow the definition (zero: O = mean of V)."""
     _announce("scale sign/zero")
