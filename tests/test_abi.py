@@ -162,6 +162,21 @@ def test_calls_without_query_rows_launch_nothing():
     assert fa.attn_fwd(*args, -1, 32, 2, 128, 128, 256, 0.0625, fa.ATTN_F16) == -2
 
 
+def test_header_is_plain_c(tmp_path):
+    # include/attn.h compiles as strict C99 and a C program links against libattn.so and
+    # runs the GPU-free entry points (tests/c/abi_from_c.c)
+    import subprocess
+    exe = str(tmp_path / "abi_from_c")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "abi_from_c.c")
+    libdir = os.path.dirname(fa.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I" + os.path.join(ROOT, "include"), src, "-o", exe, "-L" + libdir,
+                    "-lattn", "-Wl,-rpath," + libdir], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_from_c: ok" in r.stdout
+
+
 def test_binding_output_check():
     # the check fa.fwd applies to caller-provided outputs (pure Python, CPU tensors here)
     import torch
