@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 
 # MI355X dense fp16/bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU (AMD's 2.5 PFLOP/s).
 PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 METRIC = "attn fwd TFLOPS & % of MFMA peak, GQA 32Q/2KV HD=256 16Kx16K fp16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "flash_attention_amd", "csrc", f)
@@ -49,6 +50,12 @@ def visible_pairs(Lq, Lk, causal):
 def flops_workload(w):
     """4*D flops per visible (row, key) pair: 4*B*Hq*Lq*Lk*D without a mask."""
     return 4 * w.B * w.Hq * visible_pairs(w.Lq, w.Lk, w.causal) * w.D
+
+
+def algorithmic_bytes(w):
+    """Q and O (16-bit), K and V (16-bit, once per key/value head), LSE (fp32)."""
+    q = w.B * w.Hq * w.Lq * w.D * 2
+    return 2 * q + 2 * (w.B * w.Hkv * w.Lk * w.D * 2) + w.B * w.Hq * w.Lq * 4
 
 
 def flops_pages(q_len, kv_len, hd, heads_q, batch=1):
@@ -329,10 +336,22 @@ def main():
         "cpu_baseline": None,
     }
     traffic = measured_traffic(name)
-    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
-                       "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
-                       "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
-                       "algorithmic_flops_per_launch": flops}
+    # The bound follows the arithmetic intensity over the algorithmic bytes (Q, K, V, O and
+    # LSE once; a split's partial results are not the method's bytes): below the machine
+    # balance (peak flop/s over HBM bytes/s) HBM bounds the step, above it the MFMAs.
+    abytes = algorithmic_bytes(w)
+    if flops / abytes < PEAK_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gbs = abytes / (kern_avg * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                           "traffic": traffic, "algorithmic_bytes_per_launch": abytes,
+                           "algorithmic_flops_per_launch": flops}
+    else:
+        out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
+                           "peak": round(PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
+                           "algorithmic_flops_per_launch": flops,
+                           "algorithmic_bytes_per_launch": abytes}
 
     if not args.no_cpu:
         import oracle
