@@ -11,10 +11,12 @@
 // Work decomposition.  The G = Hq/Hkv query heads that read one key/value head are
 // adjacent in Q, O and LSE, so the host hands them over as one block of G*Lq query rows
 // (the grouped-query head map h -> h / G becomes row block -> key/value head).  A workgroup
-// is 4 wavefronts and owns BLOCK_M = 128*QB rows of such a block and one range of keys
-// (the whole sequence, or one split of it); each wavefront owns 32*QB whole rows, so a
-// row's max and sum never cross wavefronts.  Under the causal mask a row's position in
-// its own head is its index modulo Lq.
+// owns BLOCK_M rows of such a block and one range of keys (the whole sequence, or one split
+// of it); each wavefront owns 32*QB whole rows, so a row's max and sum never cross
+// wavefronts.  BLOCK_M is 256 (the wide shape), or 128 (the narrow shape: four wavefronts
+// of one 32-row block) when a key/value group has no more rows than that, as with
+// decode-sized queries, so that the matrix work is not spent on rows that do not exist.
+// Under the causal mask a row's position in its own head is its index modulo Lq.
 //
 // Transposed scores.  Each wavefront computes S^T = K * Q^T with K as the MFMA A operand
 // (32 keys x 16 dims) and Q^T as the B operand (16 dims x 32 queries, register resident
@@ -231,15 +233,18 @@ __device__ __forceinline__ void lds_dma16_so(i32x4 rsrc, uint32_t voffset, uint3
 // denominator share m.
 constexpr float kGrowth = 32768.0f;
 
-template <int D, typename T, bool NEG>
-__global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Params p) {
-  constexpr int QB = attn_cfg::Tile<D>::QB;
-  constexpr int BN = attn_cfg::Tile<D>::BN;
-  constexpr int NSTAGE = attn_cfg::Tile<D>::STAGES;
+// V selects the tile shape (attn_config.h): 0 wide, 1 narrow.  The second launch bound is
+// the number of wavefronts that share a SIMD, which caps the registers of one wavefront.
+template <int D, int V, typename T, bool NEG>
+__global__ __launch_bounds__((attn_cfg::threads<D, V>()), (attn_cfg::waves_per_simd<D, V>()))
+void attn_fwd_kernel(Params p) {
+  constexpr int QB = attn_cfg::Tile<D, V>::QB;
+  constexpr int BN = attn_cfg::Tile<D, V>::BN;
+  constexpr int NSTAGE = attn_cfg::Tile<D, V>::STAGES;
   static_assert(BN == 32 && (QB == 1 || QB == 2), "one or two 32-row query blocks per wave, "
                 "one 32-key block per tile");
-  constexpr int THREADS = attn_cfg::threads<D>();
-  constexpr int WAVES = attn_cfg::Tile<D>::WAVES;
+  constexpr int THREADS = attn_cfg::threads<D, V>();
+  constexpr int WAVES = attn_cfg::Tile<D, V>::WAVES;
   static_assert(NSTAGE == 4, "tiles t-1 (V), t (K), t+1, t+2 (in flight) resident");
   constexpr int KS = D / 16;    // contraction steps of S^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
@@ -248,7 +253,7 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
   constexpr int LOADS = BN * CPR / THREADS;     // 16-byte copies per thread per tile
   constexpr int ROWS_PER_LOAD = THREADS / CPR;  // tile rows one copy round covers
   static_assert(LOADS >= 1 && BN * CPR % THREADS == 0, "whole copy rounds per tile");
-  constexpr int BM = attn_cfg::block_m<D>();
+  constexpr int BM = attn_cfg::block_m<D, V>();
   constexpr int NSTEP = 2 * DB;  // P.V steps per tile, QB MFMAs (one per query block) each
   constexpr int NELEM = 16 * QB;  // scores per lane per tile
   constexpr int VPRE = 2;        // S^T steps before the end at which the first V reads issue
@@ -403,7 +408,7 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
   // With two wavefronts per SIMD (HD=128) a wavefront has 256 registers, which the compiler
   // splits evenly between VGPRs and AGPRs once AGPRs are in use; the Q^T fragments, read
   // only by the S^T MFMAs, then live in AGPRs next to the output accumulator.
-  constexpr bool Q_AGPR = WAVES > 4;
+  constexpr bool Q_AGPR = attn_cfg::waves_per_simd<D, V>() > 1;
   // Q^T operand fragments, register resident for the whole key loop: lane l holds query
   // row l%32 of block qb, dims 16*kk + 8*(l/32) .. +7.  Rows past Lq re-read row Lq-1
   // (never stored).
@@ -854,13 +859,14 @@ __global__ __launch_bounds__(attn_cfg::threads<D>(), 1) void attn_fwd_kernel(Par
   }
 }
 
-template <int D, typename T>
+template <int D, int V, typename T>
 int launch(const Params& prm, int64_t grid, hipStream_t stream) {
   constexpr int lds =
-      attn_cfg::lds_bytes(D, attn_cfg::Tile<D>::BN, attn_cfg::Tile<D>::STAGES);
-  static_assert(lds <= 160 * 1024, "LDS budget of one CU exceeded");
-  const void* fn = prm.c < 0.f ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, true>)
-                               : reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, false>);
+      attn_cfg::lds_bytes(D, attn_cfg::Tile<D, V>::BN, attn_cfg::Tile<D, V>::STAGES);
+  static_assert(lds * attn_cfg::Tile<D, V>::WG_PER_CU <= 160 * 1024,
+                "LDS budget of one CU exceeded");
+  const void* fn = prm.c < 0.f ? reinterpret_cast<const void*>(&attn_fwd_kernel<D, V, T, true>)
+                               : reinterpret_cast<const void*>(&attn_fwd_kernel<D, V, T, false>);
   // The LDS size above the default limit is a per-device attribute of the kernel: set it
   // the first time a device launches this instantiation (one bit per device; a device past
   // the 64th sets it on every launch).
@@ -869,9 +875,9 @@ int launch(const Params& prm, int64_t grid, hipStream_t stream) {
   if (hipGetDevice(&dev) != hipSuccess) return ATTN_E_LAUNCH;
   const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
   if (bit == 0 || (lds_ready.load(std::memory_order_acquire) & bit) == 0) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, false>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, V, T, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, T, true>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_fwd_kernel<D, V, T, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
       return ATTN_E_LAUNCH;
     lds_ready.fetch_or(bit, std::memory_order_release);
@@ -879,7 +885,7 @@ int launch(const Params& prm, int64_t grid, hipStream_t stream) {
   Params local = prm;
   void* args[] = {&local};
   const hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)),
-                                       dim3(attn_cfg::threads<D>()), args, lds, stream);
+                                       dim3(attn_cfg::threads<D, V>()), args, lds, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
@@ -932,12 +938,25 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
   return prm;
 }
 
-int launch_attn(const Params& prm, int64_t D, int in_dtype, int64_t grid, hipStream_t s) {
+// The planner's tile shape, told apart by its rows per workgroup (attn_plan_t.block_m).
+static_assert(attn_cfg::block_m<128, 1>() == attn_cfg::block_m<256, 1>() &&
+                  attn_cfg::block_m<128, 0>() == attn_cfg::block_m<256, 0>() &&
+                  attn_cfg::block_m<128, 1>() < attn_cfg::block_m<128, 0>(),
+              "one row count per tile shape");
+
+template <int V>
+int launch_v(const Params& prm, int64_t D, int in_dtype, int64_t grid, hipStream_t s) {
   if (D == 128)
-    return in_dtype == ATTN_F16 ? launch<128, _Float16>(prm, grid, s)
-                                : launch<128, __bf16>(prm, grid, s);
-  return in_dtype == ATTN_F16 ? launch<256, _Float16>(prm, grid, s)
-                              : launch<256, __bf16>(prm, grid, s);
+    return in_dtype == ATTN_F16 ? launch<128, V, _Float16>(prm, grid, s)
+                                : launch<128, V, __bf16>(prm, grid, s);
+  return in_dtype == ATTN_F16 ? launch<256, V, _Float16>(prm, grid, s)
+                              : launch<256, V, __bf16>(prm, grid, s);
+}
+
+int launch_attn(const Params& prm, int64_t D, int in_dtype, int block_m, int64_t grid,
+                hipStream_t s) {
+  return block_m == attn_cfg::block_m<128, 1>() ? launch_v<1>(prm, D, in_dtype, grid, s)
+                                                : launch_v<0>(prm, D, in_dtype, grid, s);
 }
 
 }  // namespace
@@ -954,7 +973,8 @@ int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float*
   attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
   const Params prm = make_params(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D,
                                  scale, 0, 1, plan.block_m);
-  return launch_attn(prm, D, in_dtype, plan.grid, static_cast<hipStream_t>(stream));
+  return launch_attn(prm, D, in_dtype, plan.block_m, plan.grid,
+                     static_cast<hipStream_t>(stream));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -975,7 +995,8 @@ int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
   attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
   const Params prm = make_params(q, k, v, nullptr, nullptr, o_part, lse_part, B, Hq, Hkv, Lq,
                                  Lk, D, scale, flags, nsplit, plan.block_m);
-  return launch_attn(prm, D, in_dtype, plan.grid * nsplit, static_cast<hipStream_t>(stream));
+  return launch_attn(prm, D, in_dtype, plan.block_m, plan.grid * nsplit,
+                     static_cast<hipStream_t>(stream));
 }
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -997,7 +1018,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   if (nsplit == 1) {
     const Params prm = make_params(q, k, v, o, lse, nullptr, nullptr, B, Hq, Hkv, Lq, Lk, D,
                                    scale, flags, 1, plan.block_m);
-    return launch_attn(prm, D, in_dtype, plan.grid, s);
+    return launch_attn(prm, D, in_dtype, plan.block_m, plan.grid, s);
   }
   // Split keys: partial results into the workspace, then the merge.
   const int64_t need = attn_workspace_bytes(B, Hq, Lq, D, nsplit);
@@ -1018,7 +1039,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + obytes);
   const Params prm = make_params(q, k, v, nullptr, nullptr, o_part, lse_part, B, Hq, Hkv, Lq,
                                  Lk, D, scale, flags, nsplit, plan.block_m);
-  rc = launch_attn(prm, D, in_dtype, plan.grid * nsplit, s);
+  rc = launch_attn(prm, D, in_dtype, plan.block_m, plan.grid * nsplit, s);
   if (rc != ATTN_OK) return rc;
   return attn_merge(o_part, lse_part, nsplit, rows, D, o, lse, in_dtype, stream);
 }

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 
 #include "../../include/attn.h"
@@ -21,38 +22,51 @@ bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
 }
 
 struct PlanInternal {
-  int waves, qb, bn, stages, block_m, lds;
+  int waves, qb, bn, stages, block_m, lds, wg_per_cu, variant;
 };
 
-bool plan_for_d(int64_t D, PlanInternal* p);
+// Tile shape for a key/value group of G*Lq query rows: the narrow shape (128 rows per
+// workgroup) when the whole group fits in it, the wide one (256 rows) otherwise.
+int variant_for(int64_t Hq, int64_t Hkv, int64_t Lq) {
+  return Hq / Hkv * Lq <= attn_cfg::kNarrowRows ? 1 : 0;
+}
+
+template <int D, int V>
+void fill_internal(PlanInternal* p) {
+  using T = attn_cfg::Tile<D, V>;
+  p->waves = T::WAVES;
+  p->qb = T::QB;
+  p->bn = T::BN;
+  p->stages = T::STAGES;
+  p->block_m = attn_cfg::block_m<D, V>();
+  p->wg_per_cu = T::WG_PER_CU;
+  p->variant = V;
+  p->lds = attn_cfg::lds_bytes(D, T::BN, T::STAGES);
+}
+
+bool plan_for(int64_t D, int v, PlanInternal* p) {
+  if (D == 128) {
+    if (v) fill_internal<128, 1>(p);
+    else fill_internal<128, 0>(p);
+  } else if (D == 256) {
+    if (v) fill_internal<256, 1>(p);
+    else fill_internal<256, 0>(p);
+  } else {
+    return false;
+  }
+  return true;
+}
+
+bool plan_for_problem(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D, PlanInternal* p) {
+  return plan_for(D, variant_for(Hq, Hkv, Lq), p);
+}
 
 // Workgroups per batch entry and key split: the G = Hq/Hkv query heads of a key/value head
 // are one block of G*Lq query rows (adjacent in memory), cut into tiles of block_m rows.
 int64_t query_tiles(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D) {
   PlanInternal p;
-  plan_for_d(D, &p);
+  plan_for_problem(Hq, Hkv, Lq, D, &p);
   return (Hq / Hkv * Lq + p.block_m - 1) / p.block_m * Hkv;
-}
-
-bool plan_for_d(int64_t D, PlanInternal* p) {
-  using namespace attn_cfg;
-  if (D == 128) {
-    p->waves = Tile<128>::WAVES;
-    p->qb = Tile<128>::QB;
-    p->bn = Tile<128>::BN;
-    p->stages = Tile<128>::STAGES;
-    p->block_m = block_m<128>();
-  } else if (D == 256) {
-    p->waves = Tile<256>::WAVES;
-    p->qb = Tile<256>::QB;
-    p->bn = Tile<256>::BN;
-    p->stages = Tile<256>::STAGES;
-    p->block_m = block_m<256>();
-  } else {
-    return false;
-  }
-  p->lds = lds_bytes(static_cast<int>(D), p->bn, p->stages);
-  return true;
 }
 
 // Sizes may be zero: B, Hq or Lq = 0 leaves no query row (nothing to do), Lk = 0 leaves
@@ -85,21 +99,22 @@ int64_t split_len_of(int64_t Lk, int64_t nsplit) {
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // Cost model of the planner, in units of one key tile (32 keys) of one workgroup.  The GPU
-// runs one workgroup per compute unit (256 of them); a workgroup costs its key tiles plus
-// a fixed overhead for pipeline fill, drain and epilogue; splitting adds the partial
-// results' round trip through HBM and a second launch.
+// runs wg_per_cu workgroups on each of its 256 compute units; a workgroup costs its key
+// tiles plus a fixed overhead for pipeline fill, drain and epilogue; splitting adds the
+// partial results' round trip through HBM and a second launch.
 double split_cost(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                  int64_t ns, int block_m) {
+                  int64_t ns, const PlanInternal& p) {
   constexpr double kCUs = 256, kOverheadTiles = 4, kLaunchTiles = 3;
+  const double slots = kCUs * p.wg_per_cu;
   const int64_t len = split_len_of(Lk, ns);
   const int64_t used = (Lk + len - 1) / len;  // splits with keys
-  const int64_t wg = (Hq / Hkv * Lq + block_m - 1) / block_m * Hkv * B * used;
-  const double rounds = std::ceil(static_cast<double>(wg) / kCUs);
+  const int64_t wg = (Hq / Hkv * Lq + p.block_m - 1) / p.block_m * Hkv * B * used;
+  const double rounds = std::ceil(static_cast<double>(wg) / slots);
   double cost = rounds * (static_cast<double>(len) / 32.0 + kOverheadTiles);
   if (ns > 1) {
-    // One tile of one workgroup: block_m x 32 x D x 4 flop at ~1/256 of ~1.2 PFLOP/s; the
+    // One tile of one workgroup: block_m x 32 x D x 4 flop at ~1/slots of ~1.2 PFLOP/s; the
     // partials are written and read in fp32 and the output written once, at ~4 TB/s.
-    const double tile_s = static_cast<double>(block_m) * 32.0 * D * 4.0 / (1.2e15 / kCUs);
+    const double tile_s = static_cast<double>(p.block_m) * 32.0 * D * 4.0 / (1.2e15 / slots);
     const double bytes = static_cast<double>(B * Hq * Lq) * D * (8.0 * used + 2.0);
     cost += bytes / 4e12 / tile_s + kLaunchTiles;
   }
@@ -107,13 +122,13 @@ double split_cost(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, in
 }
 
 int64_t choose_nsplit(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                      int block_m) {
+                      const PlanInternal& p) {
   int64_t best = 1;
   if (B * Hq * Lq == 0 || Lk == 0) return best;  // no rows or no keys: nothing to spread
-  double best_cost = split_cost(B, Hq, Hkv, Lq, Lk, D, 1, block_m);
+  double best_cost = split_cost(B, Hq, Hkv, Lq, Lk, D, 1, p);
   for (int64_t ns = 2; ns <= 128; ++ns) {
     if (split_len_of(Lk, ns) < 256) break;  // splits shorter than 8 tiles do not pay
-    const double c = split_cost(B, Hq, Hkv, Lq, Lk, D, ns, block_m);
+    const double c = split_cost(B, Hq, Hkv, Lq, Lk, D, ns, p);
     if (c < 0.95 * best_cost) {  // a split must win clearly
       best = ns;
       best_cost = c;
@@ -122,26 +137,24 @@ int64_t choose_nsplit(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   return best;
 }
 
-const char* kernel_name(int64_t D, int in_dtype, uint32_t flags) {
-  const bool c = (flags & ATTN_CAUSAL) != 0;
-  if (D == 128)
-    return in_dtype == ATTN_F16 ? (c ? "attn_fwd_d128_f16_causal" : "attn_fwd_d128_f16")
-                                : (c ? "attn_fwd_d128_bf16_causal" : "attn_fwd_d128_bf16");
-  return in_dtype == ATTN_F16 ? (c ? "attn_fwd_d256_f16_causal" : "attn_fwd_d256_f16")
-                              : (c ? "attn_fwd_d256_bf16_causal" : "attn_fwd_d256_bf16");
+// attn_fwd_d<D>_<dtype>[_causal][_m128] (_m128: the narrow 128-row shape)
+void kernel_name(int64_t D, int in_dtype, uint32_t flags, int variant, char* out, size_t n) {
+  std::snprintf(out, n, "attn_fwd_d%d_%s%s%s", static_cast<int>(D),
+                in_dtype == ATTN_F16 ? "f16" : "bf16", (flags & ATTN_CAUSAL) ? "_causal" : "",
+                variant ? "_m128" : "");
 }
 
 int fill_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
               int in_dtype, uint32_t flags, int64_t nsplit, attn_plan_t* plan) {
   PlanInternal p;
-  plan_for_d(D, &p);
+  plan_for_problem(Hq, Hkv, Lq, D, &p);
   plan->block_m = p.block_m;
   plan->block_n = p.bn;
   plan->waves = p.waves;
   plan->lds_bytes = p.lds;
   plan->grid = query_tiles(Hq, Hkv, Lq, D) * B * nsplit;
   std::memset(plan->kernel, 0, sizeof plan->kernel);
-  std::strncpy(plan->kernel, kernel_name(D, in_dtype, flags), sizeof plan->kernel - 1);
+  kernel_name(D, in_dtype, flags, p.variant, plan->kernel, sizeof plan->kernel);
   plan->nsplit = static_cast<int32_t>(nsplit);
   plan->split_len = static_cast<int32_t>(nsplit == 1 ? Lk : split_len_of(Lk, nsplit));
   plan->workspace_bytes = attn_workspace_bytes(B, Hq, Lq, D, nsplit);
@@ -287,8 +300,8 @@ int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int
   int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype);
   if (rc != ATTN_OK) return rc;
   PlanInternal p;
-  plan_for_d(D, &p);
-  int64_t ns = choose_nsplit(B, Hq, Hkv, Lq, Lk, D, p.block_m);
+  plan_for_problem(Hq, Hkv, Lq, D, &p);
+  int64_t ns = choose_nsplit(B, Hq, Hkv, Lq, Lk, D, p);
   while (ns > 1 && check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, ns) != ATTN_OK) --ns;
   return fill_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, ns, plan);
 }

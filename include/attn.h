@@ -139,7 +139,8 @@ typedef struct {
   int32_t waves;      /* 64-lane wavefronts per workgroup */
   int32_t lds_bytes;  /* LDS per workgroup */
   int64_t grid;       /* workgroups of the attention launch */
-  char kernel[64];
+  char kernel[64];    /* attn_fwd_d<D>_<f16|bf16>[_causal][_m128]; _m128: the narrow shape of
+                         128 rows per workgroup, used when (Hq/Hkv)*Lq <= 128 */
   int32_t nsplit;     /* key splits (1: no merge launch) */
   int32_t split_len;  /* keys per split (the last one may be shorter) */
   int64_t workspace_bytes; /* attn_workspace_bytes for nsplit */

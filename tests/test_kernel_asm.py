@@ -52,7 +52,7 @@ def kernels(text, which="attn_(?:fwd|merge)_kernel"):
 
 def test_all_kernels_present(asm):
     ks = kernels(asm, "attn_fwd_kernel")
-    assert len(ks) == 8, sorted(ks)  # D in {128,256} x {f16,bf16} x scale sign
+    assert len(ks) == 16, sorted(ks)  # D in {128,256} x tile shape x {f16,bf16} x scale sign
     assert len(kernels(asm, "attn_merge_kernel")) == 3  # output fp16, bf16, fp32
 
 
