@@ -79,6 +79,8 @@ WORKLOADS = {
     # and the planner splits the keys
     "decode16x16k_d256": Workload("decode16x16k_d256", 4, 32, 2, 16, 16384, 256, "f16",
                                   seed_base=8000, causal=True, nsplit=0),
+    "decode1x64k_d128_bf16": Workload("decode1x64k_d128_bf16", 1, 32, 8, 1, 65536, 128,
+                                      "bf16", seed_base=9000, causal=True, nsplit=0),
 }
 HEADLINE = "gqa16k_d256"
 

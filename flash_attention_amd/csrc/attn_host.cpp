@@ -239,9 +239,10 @@ int attn_validate_merge(const float* o_part, const float* lse_part, int64_t nspl
   if (out_dtype != ATTN_F16 && out_dtype != ATTN_BF16 && out_dtype != ATTN_F32)
     return ATTN_E_DTYPE;
   const int64_t lim = (int64_t(1) << 31) - 1;
-  // part offsets (s * rows + row) * D stay below 2^62; blocks of 256 threads below 2^31
+  // part offsets (s * rows + row) * D stay below 2^62; workgroups (64 chunks of 4
+  // elements each) below 2^31
   if (rows > (int64_t(1) << 40) / D / nsplit) return ATTN_E_SHAPE;
-  if ((rows * (D / 4) + 255) / 256 > lim) return ATTN_E_SHAPE;  // 4 elements per thread
+  if ((rows * (D / 4) + 63) / 64 > lim) return ATTN_E_SHAPE;
   auto mis16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
   if (mis16(o_part) || mis16(o)) return ATTN_E_ALIGN;
   if ((reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0) return ATTN_E_ALIGN;

@@ -12,8 +12,13 @@
 //
 // Memory-bound: every partial element is read once and every output element written once.
 // One thread owns 4 consecutive elements of one row (one 16-byte load per part, one 8- or
-// 16-byte store), so a wavefront reads 1 KiB of contiguous bytes per part; the loads of
-// four parts are issued together, so that a thread has several in flight.  The row's LSE
+// 16-byte store), so a wavefront reads 1 KiB of contiguous bytes per part, with the loads
+// of four parts issued together.  When there are few rows (decode-sized queries split over
+// many key ranges) one wavefront per 64 output chunks would walk all parts one batch after
+// another on a handful of compute units; then the parts are dealt to the PG wavefronts of
+// a workgroup (part s to wavefront s % PG).  Each wavefront weighs its parts against the
+// largest LSE among them; the PG partial sums meet in LDS, rescaled to the common maximum
+// and added in a fixed order, so the result does not depend on timing.  The row's LSE
 // values are read by all of its threads (the same cache lines).
 #include <hip/hip_runtime.h>
 
@@ -27,9 +32,9 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMergeThreads = 256;
-constexpr int kVec = 4;    // output elements per thread
-constexpr int kBatch = 4;  // parts whose loads are issued together
+constexpr int kVec = 4;     // output elements per thread
+constexpr int kBatch = 4;   // parts whose loads are issued together
+constexpr int kMaxPG = 16;  // wavefronts sharing the parts of 64 chunks
 
 struct MergeParams {
   const float* __restrict__ o_part;   // [P][rows][D]
@@ -41,35 +46,42 @@ struct MergeParams {
   int D, nparts;
 };
 
-template <int OUT>  // ATTN_F16, ATTN_BF16 or ATTN_F32
-__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeParams p) {
-  const int64_t chunk = static_cast<int64_t>(blockIdx.x) * kMergeThreads + threadIdx.x;
-  if (chunk >= p.chunks) return;
+template <int OUT, int PG>  // OUT: ATTN_F16, ATTN_BF16 or ATTN_F32; PG: wavefronts per chunk
+__global__ __launch_bounds__(64 * PG) void attn_merge_kernel(MergeParams p) {
+  __shared__ f32x4 red_acc[PG > 1 ? PG - 1 : 1][64];
+  __shared__ float red_sum[PG > 1 ? PG - 1 : 1][64];
+  __shared__ float red_top[PG > 1 ? PG - 1 : 1][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;  // this wavefront takes parts wave, wave + PG, ...
+  const int64_t chunk = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool live = chunk < p.chunks;
   const int cpr = p.D / kVec;
-  const int64_t row = chunk / cpr;
+  const int64_t row = live ? chunk / cpr : 0;
   const int col = static_cast<int>(chunk - row * cpr) * kVec;
   const float* lse_row = p.lse_part + row;  // part s at lse_row[s * rows]
 
+  // The largest LSE among this wavefront's parts (all parts when PG = 1); the PG partial
+  // sums, each relative to its own maximum, are rescaled to the common one when they meet.
   float top = -__builtin_inff();
-  for (int s = 0; s < p.nparts; ++s) top = fmaxf(top, lse_row[s * p.rows]);
+  if (live)
+    for (int s = wave; s < p.nparts; s += PG) top = fmaxf(top, lse_row[s * p.rows]);
 
+  // weights relative to the largest part: exp(LSE_s - top) <= 1 (0 for an empty part),
+  // their sum >= 1; the partial outputs are summed unnormalised and scaled once
+  constexpr float kLog2e = 1.4426950408889634f;
   f32x4 acc = {0, 0, 0, 0};
-  float lse = -__builtin_inff();
-  if (top != -__builtin_inff()) {
-    // weights relative to the largest part: exp(LSE_s - top) <= 1 (0 for an empty part),
-    // their sum >= 1; the partial outputs are summed unnormalised and scaled once
-    constexpr float kLog2e = 1.4426950408889634f;
-    float sum = 0.f;
+  float sum = 0.f;
+  if (live && top != -__builtin_inff()) {
     const float* src = p.o_part + row * p.D + col;
     const int64_t step = p.rows * p.D;  // one part
-    int s = 0;
-    for (; s + kBatch <= p.nparts; s += kBatch) {
+    int s = wave;
+    for (; s + (kBatch - 1) * PG < p.nparts; s += kBatch * PG) {
       f32x4 x[kBatch];
       float w[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        x[j] = *reinterpret_cast<const f32x4*>(src + (s + j) * step);
-        w[j] = __builtin_amdgcn_exp2f((lse_row[(s + j) * p.rows] - top) * kLog2e);
+        x[j] = *reinterpret_cast<const f32x4*>(src + (s + j * PG) * step);
+        w[j] = __builtin_amdgcn_exp2f((lse_row[(s + j * PG) * p.rows] - top) * kLog2e);
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
@@ -78,11 +90,43 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeParams p
         sum += w[j];
       }
     }
-    for (; s < p.nparts; ++s) {
+    for (; s < p.nparts; s += PG) {
       const float w = __builtin_amdgcn_exp2f((lse_row[s * p.rows] - top) * kLog2e);
       if (w != 0.f) acc += w * *reinterpret_cast<const f32x4*>(src + s * step);
       sum += w;
     }
+  }
+  if constexpr (PG > 1) {
+    if (wave > 0) {
+      red_acc[wave - 1][lane] = acc;
+      red_sum[wave - 1][lane] = sum;
+      red_top[wave - 1][lane] = top;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    float all = top;
+#pragma unroll
+    for (int w = 0; w < PG - 1; ++w) all = fmaxf(all, red_top[w][lane]);
+    if (all != -__builtin_inff()) {
+      // sums relative to top -> relative to all: factor exp(top - all) <= 1 (0 for a
+      // wavefront whose parts are all empty, whose sums are 0 anyway)
+      const float f0 = top == -__builtin_inff() ? 0.f
+                                                : __builtin_amdgcn_exp2f((top - all) * kLog2e);
+      acc *= f0;
+      sum *= f0;
+#pragma unroll
+      for (int w = 0; w < PG - 1; ++w) {
+        const float tw = red_top[w][lane];
+        const float f = tw == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((tw - all) * kLog2e);
+        acc += f * red_acc[w][lane];
+        sum += f * red_sum[w][lane];
+      }
+    }
+    top = all;
+  }
+  if (!live) return;
+  float lse = -__builtin_inff();
+  if (top != -__builtin_inff()) {
     acc *= 1.0f / sum;
     lse = top + __builtin_logf(sum);
   }
@@ -97,6 +141,26 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(MergeParams p
         __builtin_convertvector(acc, bf16x4);
   }
   if (p.lse && col == 0) p.lse[row] = lse;
+}
+
+template <int OUT>
+const void* merge_fn(int pg) {
+  switch (pg) {
+    case 16: return reinterpret_cast<const void*>(&attn_merge_kernel<OUT, 16>);
+    case 8: return reinterpret_cast<const void*>(&attn_merge_kernel<OUT, 8>);
+    case 4: return reinterpret_cast<const void*>(&attn_merge_kernel<OUT, 4>);
+    case 2: return reinterpret_cast<const void*>(&attn_merge_kernel<OUT, 2>);
+    default: return reinterpret_cast<const void*>(&attn_merge_kernel<OUT, 1>);
+  }
+}
+
+// Wavefronts per 64 output chunks: doubled while the whole launch has fewer than ~2048
+// wavefronts (a few per SIMD) and every wavefront still gets a full batch of parts.
+int part_groups(int64_t chunks, int64_t nparts) {
+  const int64_t waves = (chunks + 63) / 64;
+  int pg = 1;
+  while (pg < kMaxPG && waves * pg < 2048 && nparts >= 2 * pg * kBatch) pg *= 2;
+  return pg;
 }
 
 }  // namespace
@@ -116,12 +180,13 @@ extern "C" int attn_merge(const float* o_part, const float* lse_part, int64_t ns
   p.chunks = rows * (D / kVec);
   p.D = static_cast<int>(D);
   p.nparts = static_cast<int>(nsplit);
-  const dim3 grid(static_cast<unsigned>((p.chunks + kMergeThreads - 1) / kMergeThreads));
+  const int pg = part_groups(p.chunks, p.nparts);
+  const dim3 grid(static_cast<unsigned>((p.chunks + 63) / 64));
   hipStream_t s = static_cast<hipStream_t>(stream);
   void* args[] = {&p};
-  const void* fn = out_dtype == ATTN_F16    ? reinterpret_cast<const void*>(&attn_merge_kernel<ATTN_F16>)
-                   : out_dtype == ATTN_BF16 ? reinterpret_cast<const void*>(&attn_merge_kernel<ATTN_BF16>)
-                                            : reinterpret_cast<const void*>(&attn_merge_kernel<ATTN_F32>);
-  const hipError_t e = hipLaunchKernel(fn, grid, dim3(kMergeThreads), args, 0, s);
+  const void* fn = out_dtype == ATTN_F16    ? merge_fn<ATTN_F16>(pg)
+                   : out_dtype == ATTN_BF16 ? merge_fn<ATTN_BF16>(pg)
+                                            : merge_fn<ATTN_F32>(pg);
+  const hipError_t e = hipLaunchKernel(fn, grid, dim3(64 * pg), args, 0, s);
   return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }

@@ -167,6 +167,35 @@ def test_merge_kernel_matches_oracle(D, out):
     assert np.abs(lg[fin] - lse_ref[fin]).max() <= 1e-5 * 30, np.abs(lg[fin] - lse_ref[fin]).max()
 
 
+@pytest.mark.parametrize("P,rows,D", [(8, 3, 128), (16, 1, 256), (33, 7, 136), (64, 40, 128),
+                                      (130, 5, 256), (256, 1, 128), (256, 300, 8)])
+def test_merge_many_parts_few_rows(P, rows, D):
+    """Decode-sized merges (many key ranges, few rows), where the parts are dealt over
+    several wavefronts of a workgroup and summed in LDS: against the oracle's merge, with
+    empty parts and a row empty in every part."""
+    _announce("merge P=%d rows=%d D=%d" % (P, rows, D))
+    g = torch.Generator().manual_seed(27 + P + rows)
+    o_part = torch.randn(P, rows, D, generator=g)
+    lse_part = torch.rand(P, rows, generator=g) * 40 - 20
+    lse_part[::3, :] = -math.inf     # every third part empty
+    if rows > 1:
+        lse_part[:, rows - 1] = -math.inf  # the last row empty in every part
+    o_part[::3] = float("nan")       # an empty part's output is never read
+    dev = torch.device("cuda:0")
+    o, lse = fa.merge(o_part.to(dev), lse_part.to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.merge(torch.nan_to_num(o_part).double().numpy(),
+                                  lse_part.double().numpy())
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    if rows > 1:
+        assert not og[rows - 1].any() and lg[rows - 1] == -math.inf
+    fin = np.isfinite(lse_ref)
+    assert fin.any()
+    assert np.isfinite(og).all() and np.isfinite(lg[fin]).all()
+    assert np.abs(og - o_ref).max() <= 2e-6 * max(1.0, np.abs(o_ref).max())
+    assert np.abs(lg[fin] - lse_ref[fin]).max() <= 1e-5 * 20
+
+
 def test_merge_without_lse_and_single_part():
     """lse = NULL leaves no LSE; one part merges to itself (weight exactly 1)."""
     _announce("merge single part")
