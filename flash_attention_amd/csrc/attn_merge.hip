@@ -154,12 +154,12 @@ const void* merge_fn(int pg) {
   }
 }
 
-// Wavefronts per 64 output chunks: doubled while the whole launch has fewer than ~2048
-// wavefronts (a few per SIMD) and every wavefront still gets a full batch of parts.
+// Wavefronts per 64 output chunks: doubled while the whole launch has fewer than 4096
+// wavefronts (four per SIMD) and every wavefront still gets a full batch of parts.
 int part_groups(int64_t chunks, int64_t nparts) {
   const int64_t waves = (chunks + 63) / 64;
   int pg = 1;
-  while (pg < kMaxPG && waves * pg < 2048 && nparts >= 2 * pg * kBatch) pg *= 2;
+  while (pg < kMaxPG && waves * pg < 4096 && nparts >= 2 * pg * kBatch) pg *= 2;
   return pg;
 }
 
