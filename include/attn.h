@@ -21,7 +21,10 @@
  * Numerics.  Q, K, V are fp16 or bf16; both matrix products accumulate in
  * fp32, the softmax runs in fp32 (online/streaming over key tiles), and the
  * probabilities are rounded to the input type before the second product.
- * O is written in the input type (round to nearest even); LSE in fp32.
+ * O is written in the input type (round to nearest even); LSE in fp32.  The scores
+ * scale * q.k are formed in fp32 and must be finite there: with fp16 inputs that holds for
+ * any |scale| below about 1e26 / D; with bf16 inputs (whose range is fp32's) it is the
+ * caller's data that must keep q.k within fp32.
  *
  * Causal masking (attn_fwd_ex, flag ATTN_CAUSAL).  Query row i sees key j
  * only if j <= i + (Lk - Lq): the diagonal is aligned to the end of both
