@@ -15,11 +15,18 @@ from parity_util import scale_of
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("causal,nsplit", [(False, 1), (True, 1), (False, 4), (True, 3)])
-def test_capture_and_replay(causal, nsplit):
-    print("\n[case] graph causal=%s nsplit=%d" % (causal, nsplit), flush=True)
+WIDE = (2, 8, 2, 100, 1500, 128)   # 400 rows per key/value group: the wide tile shape
+NARROW = (1, 32, 8, 1, 8192, 128)  # decode, 4 rows per group: the narrow shape; the merge
+#                                    of 32 parts over 32 rows deals them over 8 wavefronts
+
+
+@pytest.mark.parametrize("shape,causal,nsplit", [(WIDE, False, 1), (WIDE, True, 1),
+                                                 (WIDE, False, 4), (WIDE, True, 3),
+                                                 (NARROW, True, 1), (NARROW, True, 32)])
+def test_capture_and_replay(shape, causal, nsplit):
+    print("\n[case] graph shape=%s causal=%s nsplit=%d" % (shape, causal, nsplit), flush=True)
     dev = torch.device("cuda:0")
-    B, Hq, Hkv, Lq, Lk, D = 2, 8, 2, 100, 1500, 128
+    B, Hq, Hkv, Lq, Lk, D = shape
     q, k, v = (t.to(dev) for t in attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "f16", seed=31))
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=dev)
