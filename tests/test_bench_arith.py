@@ -46,3 +46,34 @@ def test_headline_formula_and_softmax_term():
 def test_peak_is_mi355x_dense_fp16():
     # 256 CUs x 2.4 GHz x 4096 dense fp16 flop per clock per CU
     assert abs(bench.PEAK_TFLOPS - 2516.58) < 0.01
+
+
+def test_visible_pairs_brute_force():
+    # row i sees key j iff j <= i + Lk - Lq: counted pair by pair on small shapes
+    for Lq, Lk in [(5, 8), (8, 5), (7, 7), (1, 9), (9, 1), (3, 3)]:
+        brute = sum(1 for i in range(Lq) for j in range(Lk) if j <= i + Lk - Lq)
+        assert bench.visible_pairs(Lq, Lk, True) == brute, (Lq, Lk)
+        assert bench.visible_pairs(Lq, Lk, False) == Lq * Lk
+    n = 16384
+    assert bench.visible_pairs(n, n, True) == n * (n + 1) // 2
+
+
+def test_algorithmic_bytes_and_bound():
+    import attn_inputs
+    w = attn_inputs.WORKLOADS["gqa16k_d256"]
+    # Q + K + V + O (16-bit) + LSE (fp32): the 572,522,496 bytes of the headline shape
+    assert bench.algorithmic_bytes(w) == 572522496
+    balance = bench.PEAK_TFLOPS * 1e12 / (bench.PEAK_HBM_GBS * 1e9)
+    assert 314 < balance < 315
+    ai = {n: bench.flops_workload(x) / bench.algorithmic_bytes(x)
+          for n, x in attn_inputs.WORKLOADS.items()}
+    assert ai["gqa16k_d256"] > 15000 and ai["gqa8k_d128_bf16"] > balance
+    assert ai["decode16x16k_d256"] < balance and ai["decode1x64k_d128_bf16"] < 5
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
