@@ -62,6 +62,25 @@ def test_parity_workload_full_size(name):
     parity(q, k, v, w.scale, w.dtype, rows=rows, what=name, causal=w.causal, nsplit=w.nsplit)
 
 
+OTHER_DTYPE = ["gqa4k_d256", "gqa8k_d128_bf16", "rect1kx16k_d256", "gqa16k_d256",
+               "gqa16k_d256_causal"]
+
+
+@pytest.mark.parametrize("name", OTHER_DTYPE)
+def test_parity_workload_other_dtype(name):
+    """The same full-size workloads with the other 16-bit input type (fp16 <-> bf16), so
+    that both kernels of each head dimension run at the benchmark's sizes."""
+    import dataclasses
+    w = attn_inputs.WORKLOADS[name]
+    w = dataclasses.replace(w, dtype="bf16" if w.dtype == "f16" else "f16",
+                            seed_base=w.seed_base + 500)
+    _announce("%s other dtype %s" % (name, w.describe()))
+    q, k, v = attn_inputs.workload_qkv(w)
+    rows = attn_inputs.sample_rows(w, n_random=512)
+    parity(q, k, v, w.scale, w.dtype, rows=rows, what=name + " " + w.dtype, causal=w.causal,
+           nsplit=w.nsplit)
+
+
 def test_worked_example_on_gpu():
     """Two keys, D=256, scale 1/16: O = -tanh(1/2) in every coordinate, LSE = ln(1+e)."""
     _announce("worked example")
