@@ -208,6 +208,29 @@ def test_merge_without_lse_and_single_part():
     assert lse is None and torch.equal(o.cpu(), o_part[0])
 
 
+BOUNDARY = [(G, Lq, D, causal, nsplit)
+            for (G, Lq) in [(1, 127), (8, 16), (1, 129), (16, 8), (4, 33)]
+            for D in (128, 256) for causal, nsplit in ((False, 1), (True, 0))]
+
+
+@pytest.mark.parametrize("G,Lq,D,causal,nsplit", BOUNDARY)
+def test_narrow_wide_boundary(G, Lq, D, causal, nsplit):
+    """Key/value groups of 127, 128 (narrow 128-row workgroups) and 129, 132 rows (wide
+    256-row workgroups): the planner's shape choice and parity on both sides of it."""
+    B, Hkv, Lk = 2, 2, 700
+    Hq = G * Hkv
+    narrow = G * Lq <= 128
+    plan = fa.attn_plan(B, Hq, Hkv, Lq, Lk, D, fa.ATTN_F16)
+    assert plan.block_m == (128 if narrow else 256)
+    assert plan.kernel.decode().endswith("_m128") == narrow
+    seed = 14000 + G * 1000 + Lq + D
+    _announce("boundary G=%d Lq=%d rows=%d D=%d causal=%d nsplit=%d seed=%d"
+              % (G, Lq, G * Lq, D, causal, nsplit, seed))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "f16", seed=seed)
+    parity(q, k, v, scale_of(D), "f16", causal=causal, nsplit=nsplit,
+           what="boundary G=%d Lq=%d D=%d" % (G, Lq, D))
+
+
 def _random_cases(n=48, seed=20261202):
     """Seeded random mixes of every option: shapes with ragged tails, GQA ratios, both
     head dims and dtypes, causal or not, split counts (0 = the planner's), scale sign."""
