@@ -470,7 +470,13 @@ void attn_fwd_kernel(Params p) {
   // S^T(t) = K(t) Q^T, fp32 accumulation, the QB query blocks sharing each K fragment.  The
   // first two fragments arrive prefetched in kf[0..1]; the rest are fetched two steps ahead,
   // and the scheduling barriers keep the compiler from hoisting all of them (64 registers).
+  // Where two wavefronts share a SIMD (HD=128), the one in this MFMA-only phase gets the
+  // higher issue priority, so that its MFMAs go out while the other wavefront's softmax
+  // VALU work fills the gaps (measured: +1.6 % at 8K x 8K, +3.7 % of the cycles with the
+  // clock unconstrained; the level does not matter).
+  constexpr bool kShareSimd = attn_cfg::waves_per_simd<D, V>() > 1;
   auto qk = [&](const char* ks, f32x16 (&sacc)[QB], u32x4 (&kf)[3], auto&& tail_loads) {
+    if constexpr (kShareSimd) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       if (kk + 2 < KS) kf[(kk + 2) % 3] = kfrag(ks, kk + 2);
@@ -487,6 +493,7 @@ void attn_fwd_kernel(Params p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kShareSimd) __builtin_amdgcn_s_setprio(0);
   };
   // One P.V step s of a tile: V^T fragment (32 dims x 16 keys) for MFMA step s, times both
   // P^T blocks.  MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator
