@@ -58,3 +58,45 @@ def test_capture_and_replay(shape, causal, nsplit):
         x = (q.float() * 2).sum()
         torch.cuda.synchronize()
         assert torch.isfinite(x)
+
+
+def test_concurrent_calls_from_threads():
+    """Reentrancy: four host threads, each on its own stream with its own outputs, call the
+    library 10 times (one pass, causal with splits, and the merge inside); every result
+    equals the single-threaded one bit for bit."""
+    import threading
+    print("\n[case] four threads, four streams", flush=True)
+    dev = torch.device("cuda:0")
+    shapes = [(1, 8, 2, 300, 700, 128, False, 1), (2, 4, 1, 64, 2000, 256, True, 0),
+              (1, 32, 8, 1, 4096, 128, True, 0), (1, 2, 1, 513, 129, 256, True, 3)]
+    inputs, refs = [], []
+    for i, (B, Hq, Hkv, Lq, Lk, D, causal, nsplit) in enumerate(shapes):
+        q, k, v = (t.to(dev) for t in attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "bf16",
+                                                         seed=40 + i))
+        o, lse = fa.fwd(q, k, v, causal=causal, nsplit=nsplit)
+        torch.cuda.synchronize()
+        inputs.append((q, k, v, causal, nsplit))
+        refs.append((o.clone(), lse.clone()))
+    errors = []
+
+    def worker(i):
+        try:
+            q, k, v, causal, nsplit = inputs[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [fa.fwd(q, k, v, causal=causal, nsplit=nsplit, stream=s)
+                        for _ in range(10)]
+            s.synchronize()
+            for o, lse in outs:
+                if not (torch.equal(o, refs[i][0]) and torch.equal(lse, refs[i][1])):
+                    errors.append(i)
+        except Exception as e:  # reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
