@@ -77,3 +77,8 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"),
                         "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_vs_baseline_uses_the_pages_figure(figures):
+    # the pages' own TFLOPS for the headline workload (another GPU's: context only)
+    assert bench.PAGES_TFLOPS == {"gqa16k_d256": figures["headline"]["tflops"]}
