@@ -231,6 +231,27 @@ def test_narrow_wide_boundary(G, Lq, D, causal, nsplit):
            what="boundary G=%d Lq=%d D=%d" % (G, Lq, D))
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lk,D,causal,nsplit", [
+    (3000, 4, 2, 3, 37, 128, False, 1),    # many batch entries, tiny heads (narrow shape)
+    (1200, 2, 1, 70, 33, 256, True, 1),    # many batch entries, 140 rows per group (wide)
+    (2, 256, 1, 1, 3000, 128, True, 0),    # 256 query heads on one key/value head, decode
+    (1, 64, 1, 5, 5000, 256, False, 0),    # 320 rows per group over long keys, split
+])
+def test_large_batch_and_wide_groups(B, Hq, Hkv, Lq, Lk, D, causal, nsplit):
+    """Batch and head indices far from the small cases (grid ids past 10^4, block
+    renumbering over many XCD rounds) and very wide query groups, on sampled rows."""
+    seed = 15000 + B + Hq + Lq
+    _announce("large B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d causal=%d nsplit=%d seed=%d"
+              % (B, Hq, Hkv, Lq, Lk, D, causal, nsplit, seed))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "bf16", seed=seed)
+    total = B * Hq * Lq
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.choice(total, size=min(3000, total), replace=False),
+                                     [0, total - 1]])).astype(np.int64)
+    parity(q, k, v, scale_of(D), "bf16", rows=rows, causal=causal, nsplit=nsplit,
+           what="large B=%d Hq=%d" % (B, Hq))
+
+
 def _random_cases(n=48, seed=20261202):
     """Seeded random mixes of every option: shapes with ragged tails, GQA ratios, both
     head dims and dtypes, causal or not, split counts (0 = the planner's), scale sign."""
