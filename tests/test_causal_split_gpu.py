@@ -252,6 +252,42 @@ def test_large_batch_and_wide_groups(B, Hq, Hkv, Lq, Lk, D, causal, nsplit):
            what="large B=%d Hq=%d" % (B, Hq))
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lk,D,causal,nsplit", [
+    (1, 2, 1, 1, 1, 128, False, 1), (2, 4, 2, 37, 77, 128, True, 1), (1, 8, 2, 300, 500, 256,
+                                                                        False, 3),
+    (1, 16, 1, 8, 999, 256, True, 0), (3, 2, 2, 129, 31, 128, True, 2), (1, 4, 1, 1000, 64,
+                                                                          256, False, 1)])
+def test_nothing_written_outside_the_outputs(B, Hq, Hkv, Lq, Lk, D, causal, nsplit):
+    """O, LSE and the partial results sit inside larger buffers filled with a sentinel:
+    after the launches every byte before and after them still holds it (ragged tails, the
+    16-byte output stores, both tile shapes, splits and the merge)."""
+    _announce("guard bands B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d causal=%d nsplit=%d"
+              % (B, Hq, Hkv, Lq, Lk, D, causal, nsplit))
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "f16",
+                                                     seed=16000 + Lq))
+    G = 4096  # guard elements on each side (16-byte aligned for both element sizes)
+    n_o, n_l = B * Hq * Lq * D, B * Hq * Lq
+    obuf = torch.full((n_o + 2 * G,), 7.0, dtype=torch.float16, device=dev)
+    lbuf = torch.full((n_l + 2 * G,), 7.0, dtype=torch.float32, device=dev)
+    o = obuf[G:G + n_o].view(B, Hq, Lq, D)
+    lse = lbuf[G:G + n_l].view(B, Hq, Lq)
+    fa.fwd(q, k, v, out=o, lse=lse, causal=causal, nsplit=nsplit)
+    ns = max(nsplit, 2)
+    n_p, n_pl = ns * n_o, ns * n_l
+    pbuf = torch.full((n_p + 2 * G,), 7.0, dtype=torch.float32, device=dev)
+    plbuf = torch.full((n_pl + 2 * G,), 7.0, dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    rc = fa.attn_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             pbuf[G:].data_ptr(), plbuf[G:].data_ptr(), B, Hq, Hkv, Lq, Lk, D,
+                             D ** -0.5, fa.ATTN_F16, fa.ATTN_CAUSAL if causal else 0, ns, s)
+    assert rc == 0
+    torch.cuda.synchronize()
+    for buf, n in ((obuf, n_o), (lbuf, n_l), (pbuf, n_p), (plbuf, n_pl)):
+        assert bool((buf[:G] == 7).all()) and bool((buf[G + n:] == 7).all())
+    assert not bool(torch.isnan(o.float()).any())
+
+
 def _random_cases(n=48, seed=20261202):
     """Seeded random mixes of every option: shapes with ragged tails, GQA ratios, both
     head dims and dtypes, causal or not, split counts (0 = the planner's), scale sign."""
