@@ -260,12 +260,14 @@ def test_large_batch_and_wide_groups(B, Hq, Hkv, Lq, Lk, D, causal, nsplit):
 def test_nothing_written_outside_the_outputs(B, Hq, Hkv, Lq, Lk, D, causal, nsplit):
     """O, LSE and the partial results sit inside larger buffers filled with a sentinel:
     after the launches every byte before and after them still holds it (ragged tails, the
-    16-byte output stores, both tile shapes, splits and the merge)."""
+    16-byte output stores, both tile shapes, splits and the merge), and Q, K, V are
+    unchanged."""
     _announce("guard bands B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d causal=%d nsplit=%d"
               % (B, Hq, Hkv, Lq, Lk, D, causal, nsplit))
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "f16",
                                                      seed=16000 + Lq))
+    q0, k0, v0 = q.clone(), k.clone(), v.clone()
     G = 4096  # guard elements on each side (16-byte aligned for both element sizes)
     n_o, n_l = B * Hq * Lq * D, B * Hq * Lq
     obuf = torch.full((n_o + 2 * G,), 7.0, dtype=torch.float16, device=dev)
@@ -286,6 +288,7 @@ def test_nothing_written_outside_the_outputs(B, Hq, Hkv, Lq, Lk, D, causal, nspl
     for buf, n in ((obuf, n_o), (lbuf, n_l), (pbuf, n_p), (plbuf, n_pl)):
         assert bool((buf[:G] == 7).all()) and bool((buf[G + n:] == 7).all())
     assert not bool(torch.isnan(o.float()).any())
+    assert torch.equal(q, q0) and torch.equal(k, k0) and torch.equal(v, v0)  # inputs untouched
 
 
 def _random_cases(n=48, seed=20261202):
