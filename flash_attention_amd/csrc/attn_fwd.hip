@@ -36,9 +36,10 @@
 // t runs, one slice after each MFMA); tile t+1 is landing, and tile t+2 is copied after
 // the one workgroup barrier of the iteration, the waves taking turns over the last four
 // steps.  At HD=256 each wavefront owns 64 query rows (two 32-row MFMA blocks), so every
-// K and V fragment read from LDS feeds two MFMAs; at HD=128 two wavefronts of 32 rows share
-// each SIMD.  Q stays in registers and the output accumulator in pinned AGPRs for the
-// whole key loop.
+// K and V fragment read from LDS feeds two MFMAs (in the wide shape); at HD=128 two
+// wavefronts of 32 rows share each SIMD, the one in its S^T phase at the higher issue
+// priority.  Q stays in registers and the output accumulator in pinned AGPRs for the whole
+// key loop.
 #include <hip/hip_runtime.h>
 
 #include <atomic>

@@ -156,7 +156,8 @@ int attn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_
               int in_dtype, attn_plan_t* plan);
 
 /* The launch attn_fwd_ex makes with nsplit = 0 and these flags: the planner picks the number
- * of key splits from a cost model of the GPU's 256 compute units (one workgroup each), the
+ * of key splits from a cost model of the GPU's 256 compute units (one or two workgroups each,
+ * by tile shape), the
  * key range per workgroup and the merge traffic. */
 int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                  int in_dtype, uint32_t flags, attn_plan_t* plan);
