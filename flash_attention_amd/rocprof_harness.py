@@ -3,6 +3,7 @@ traffic and bandwidth of one workload, from separate profiler runs of bench.py.
 
     python -m flash_attention_amd.rocprof_harness --workload gqa16k_d256 \
         [--outdir rocprof_out] [--traffic-json traffic.json]
+    python -m flash_attention_amd.rocprof_harness --workload all --traffic-json traffic.json
 
 Runs, each as its own child process (this process never touches the GPU):
   1. rocprofv3 --kernel-trace --stats          -> launch durations of the kernel
@@ -93,13 +94,30 @@ def calibrated_bytes(outdir, name, counter):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--workload", default="gqa16k_d256")
+    ap.add_argument("--workload", default="gqa16k_d256",
+                    help="a name of attn_inputs.WORKLOADS, or 'all' (every one but 'tiny', "
+                         "each into its own subdirectory of --outdir)")
     ap.add_argument("--outdir", default="rocprof_out")
     ap.add_argument("--traffic-json", default=None)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--kill-after", type=int, default=90)
     a = ap.parse_args()
-    out = os.path.abspath(a.outdir)
+    if a.workload != "all":
+        return profile(a.workload, os.path.abspath(a.outdir), a)
+    sys.path.insert(0, ROOT)
+    import attn_inputs  # noqa: E402  (shapes only; imports no GPU code)
+    for name in attn_inputs.WORKLOADS:
+        if name == "tiny":
+            continue
+        rc = profile(name, os.path.join(os.path.abspath(a.outdir), name), a)
+        if rc != 0:
+            return rc
+    return 0
+
+
+def profile(workload, out, a):
+    """The four passes over one workload; 0, or the exit status of the pass that failed."""
+    a = argparse.Namespace(**dict(vars(a), workload=workload))
     os.makedirs(out, exist_ok=True)
     rp = "rocprofv3"
 
