@@ -74,6 +74,7 @@ struct Params {
   int64_t part_rows;  // B * Hq * Lq
   int Hq, Hkv, G, Lq, Lk;
   int n_qtiles;
+  int n_work;     // workgroups with work: n_qtiles * (row blocks) * nsplit
   int nsplit;     // key splits (workgroups per query tile)
   int split_len;  // keys per split, a multiple of the key tile (split s: [s*len, (s+1)*len))
   int diag;       // row i sees key j only if j <= i + diag (Lk - Lq if causal, else Lk)
@@ -283,6 +284,9 @@ void attn_fwd_kernel(Params p) {
   const int per = nblk >> 3, rem = nblk & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + local;
   // (integer division is expanded into VALU code; readfirstlane keeps the results in SGPRs)
+  // (a grid larger than the work, which the host never launches, would find nothing here
+  // rather than rows outside the tensors)
+  if (logical >= p.n_work) return;
   const int split = __builtin_amdgcn_readfirstlane(logical % p.nsplit);
   const int tile_id = __builtin_amdgcn_readfirstlane(logical / p.nsplit);
   int qtile = __builtin_amdgcn_readfirstlane(tile_id % p.n_qtiles);
@@ -922,6 +926,7 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
   prm.Lq = static_cast<int>(G * Lq);
   prm.Lk = static_cast<int>(Lk);
   prm.n_qtiles = static_cast<int>((G * Lq + block_m - 1) / block_m);
+  prm.n_work = static_cast<int>(prm.n_qtiles * B * Hkv * nsplit);  // < 2^31 (validated)
   prm.lq_head = static_cast<int>(Lq);
   {
     int l = 0;
@@ -1015,12 +1020,15 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                             nsplit);
   if (rc != ATTN_OK) return rc;
   if (B * Hq * Lq == 0) return ATTN_OK;  // (no workspace needed either)
+  // plan.grid: the workgroups of the attention launch, every split included (attn_plan_ex
+  // counts its splits already; attn_plan plans one pass)
   attn_plan_t plan;
   if (nsplit == 0) {
     attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, &plan);
     nsplit = plan.nsplit;
   } else {
     attn_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, &plan);
+    plan.grid *= nsplit;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (nsplit == 1) {
@@ -1047,7 +1055,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + obytes);
   const Params prm = make_params(q, k, v, nullptr, nullptr, o_part, lse_part, B, Hq, Hkv, Lq,
                                  Lk, D, scale, flags, nsplit, plan.block_m);
-  rc = launch_attn(prm, D, in_dtype, plan.block_m, plan.grid * nsplit, s);
+  rc = launch_attn(prm, D, in_dtype, plan.block_m, plan.grid, s);
   if (rc != ATTN_OK) return rc;
   return attn_merge(o_part, lse_part, nsplit, rows, D, o, lse, in_dtype, stream);
 }

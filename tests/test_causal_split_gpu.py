@@ -291,6 +291,39 @@ def test_nothing_written_outside_the_outputs(B, Hq, Hkv, Lq, Lk, D, causal, nspl
     assert torch.equal(q, q0) and torch.equal(k, k0) and torch.equal(v, v0)  # inputs untouched
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lk,D,causal", [
+    (4, 32, 2, 16, 4096, 256, True), (1, 32, 8, 1, 8192, 128, False),
+    (1, 16, 1, 8, 999, 256, True), (1, 8, 2, 200, 3000, 128, False)])
+def test_c_entry_with_planner_splits(B, Hq, Hkv, Lq, Lk, D, causal):
+    """attn_fwd_ex called through the C ABI with nsplit = 0, so that the library plans the
+    key splits itself: parity with the oracle, and O, LSE and the workspace inside sentinel
+    guard bands that no launch may touch."""
+    flags = fa.ATTN_CAUSAL if causal else 0
+    plan = fa.attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, fa.ATTN_F16, flags)
+    seed = 17000 + Lq + Lk
+    _announce("C entry nsplit=0 (planner %d) B=%d Hq=%d Hkv=%d Lq=%d Lk=%d D=%d causal=%d "
+              "seed=%d" % (plan.nsplit, B, Hq, Hkv, Lq, Lk, D, causal, seed))
+    dev = torch.device("cuda:0")
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, "f16", seed=seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    G = 65536  # guard bytes on each side
+    n_o, n_l, n_w = B * Hq * Lq * D * 2, B * Hq * Lq * 4, max(plan.workspace_bytes, 256)
+    bufs = [torch.full((n + 2 * G,), 0x5A, dtype=torch.uint8, device=dev) for n in (n_o, n_l, n_w)]
+    o_ptr, l_ptr, w_ptr = (b.data_ptr() + G for b in bufs)
+    rc = fa.attn_fwd_ex(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o_ptr, l_ptr, B, Hq, Hkv,
+                        Lq, Lk, D, D ** -0.5, fa.ATTN_F16, flags, 0, w_ptr, n_w,
+                        torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, fa.attn_strerror(rc)
+    torch.cuda.synchronize()
+    for b, n in zip(bufs, (n_o, n_l, n_w)):
+        assert bool((b[:G] == 0x5A).all()) and bool((b[G + n:] == 0x5A).all())
+    o = bufs[0][G:G + n_o].view(torch.float16).view(B, Hq, Lq, D).cpu()
+    lse = bufs[1][G:G + n_l].view(torch.float32).view(B, Hq, Lq).cpu()
+    o_ref, lse_ref = oracle.attention(q, k, v, float(np.float32(D ** -0.5)), causal=causal)
+    m = metrics(o.reshape(-1, D), lse.reshape(-1), o_ref, lse_ref)
+    check(m, "f16", "C entry nsplit=0")
+
+
 def _random_cases(n=48, seed=20261202):
     """Seeded random mixes of every option: shapes with ragged tails, GQA ratios, both
     head dims and dtypes, causal or not, split counts (0 = the planner's), scale sign."""
