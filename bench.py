@@ -220,10 +220,15 @@ def main():
     stream = torch.cuda.current_stream(dev)
     code = fa.dtype_code(q)
     flags = fa.ATTN_CAUSAL if w.causal else 0
-    # the planner's launch (kernel name, split choice); the workload may fix the split count
-    plan = fa.attn_plan_ex(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code, flags)
-    nsplit = w.nsplit if w.nsplit else plan.nsplit
-    plan.grid = fa.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code).grid * nsplit
+    # the launch: the planner's (splits and tile shape: attn_fwd_ex with nsplit = 0), unless
+    # the workload fixes the split count (then the default tile shape)
+    if w.nsplit:
+        plan = fa.attn_plan(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code)
+        plan.grid *= w.nsplit
+        plan.nsplit = w.nsplit
+    else:
+        plan = fa.attn_plan_ex(w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, code, flags)
+    nsplit = plan.nsplit
     # the workspace of a split launch is allocated once, outside the timed region
     ws_bytes = fa.attn_workspace_bytes(w.B, w.Hq, w.Lq, w.D, nsplit)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -233,8 +238,8 @@ def main():
         launch = fa.attn_fwd_stream
     else:
         args_c = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                  w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, scale, code, flags, nsplit, ws.data_ptr(),
-                  ws_bytes, stream.cuda_stream)
+                  w.B, w.Hq, w.Hkv, w.Lq, w.Lk, w.D, scale, code, flags, w.nsplit,
+                  ws.data_ptr(), ws_bytes, stream.cuda_stream)
         launch = fa.attn_fwd_ex
     torch.cuda.synchronize()
     print("[bench] %s inputs ready in %.1fs; plan %s grid=%d block_m=%d block_n=%d nsplit=%d" %

@@ -268,9 +268,11 @@ def fwd(q, k, v, scale=None, out=None, lse=None, return_lse=True, stream=None, c
         rc = attn_fwd_stream(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
                              B, Hq, Hkv, Lq, Lk, D, float(scale), dtype_code(q), s.cuda_stream)
     else:
-        if nsplit == 0:
-            nsplit = attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, dtype_code(q), flags).nsplit
-        need = attn_workspace_bytes(B, Hq, Lq, D, nsplit) if nsplit >= 1 else 0
+        # nsplit = 0 goes to the library as is: its planner picks the splits (and, for
+        # key/value groups of 129-256 rows, the tile shape); the workspace is sized from the
+        # same plan
+        need = (attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, dtype_code(q), flags).workspace_bytes
+                if nsplit == 0 else attn_workspace_bytes(B, Hq, Lq, D, nsplit))
         if need < 0:
             raise AttnError(need, attn_strerror(need))
         if workspace is None and need > 0:

@@ -23,6 +23,7 @@ bool overlaps(const void* a, uint64_t abytes, const void* b, uint64_t bbytes) {
 
 struct PlanInternal {
   int waves, qb, bn, stages, block_m, lds, wg_per_cu, variant;
+  double tile_cost;  // time of one key tile of one workgroup, in wide-shape tiles
 };
 
 // Tile shape for a key/value group of G*Lq query rows: the narrow shape (128 rows per
@@ -42,6 +43,10 @@ void fill_internal(PlanInternal* p) {
   p->wg_per_cu = T::WG_PER_CU;
   p->variant = V;
   p->lds = attn_cfg::lds_bytes(D, T::BN, T::STAGES);
+  // A narrow HD=256 workgroup does half the rows' matrix work per tile on a compute unit of
+  // its own: about 0.6 of a wide tile's time (measured).  A narrow HD=128 workgroup shares
+  // its compute unit with a second one and takes a wide tile's time.
+  p->tile_cost = (V == 1 && D == 256) ? 0.6 : 1.0;
 }
 
 bool plan_for(int64_t D, int v, PlanInternal* p) {
@@ -57,22 +62,19 @@ bool plan_for(int64_t D, int v, PlanInternal* p) {
   return true;
 }
 
-bool plan_for_problem(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D, PlanInternal* p) {
-  return plan_for(D, variant_for(Hq, Hkv, Lq), p);
-}
-
 // Workgroups per batch entry and key split: the G = Hq/Hkv query heads of a key/value head
-// are one block of G*Lq query rows (adjacent in memory), cut into tiles of block_m rows.
-int64_t query_tiles(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D) {
+// are one block of G*Lq query rows (adjacent in memory), cut into tiles of block_m rows of
+// tile shape v (-1: the default shape for the problem).
+int64_t query_tiles(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t D, int v = -1) {
   PlanInternal p;
-  plan_for_problem(Hq, Hkv, Lq, D, &p);
+  plan_for(D, v < 0 ? variant_for(Hq, Hkv, Lq) : v, &p);
   return (Hq / Hkv * Lq + p.block_m - 1) / p.block_m * Hkv;
 }
 
 // Sizes may be zero: B, Hq or Lq = 0 leaves no query row (nothing to do), Lk = 0 leaves
 // every row without keys (O = 0, LSE = -inf).  Hkv must be positive.
 int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-                int in_dtype, int64_t nsplit = 1) {
+                int in_dtype, int64_t nsplit = 1, int variant = -1) {
   if (B < 0 || Hq < 0 || Hkv <= 0 || Lq < 0 || Lk < 0 || D <= 0) return ATTN_E_SHAPE;
   if (D != 128 && D != 256) return ATTN_E_HEADDIM;
   if (Hq % Hkv != 0) return ATTN_E_GQA;
@@ -84,7 +86,7 @@ int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int6
   // the query heads of one key/value head run as one block of G*Lq rows: its row offsets
   // fit in int32 too
   if (Lq > 0 && Hq / Hkv > lim / D / Lq) return ATTN_E_SHAPE;
-  const int64_t groups = query_tiles(Hq, Hkv, Lq, D);  // workgroups per (b, split)
+  const int64_t groups = query_tiles(Hq, Hkv, Lq, D, variant);  // workgroups per (b, split)
   if (B > 0 && (groups > lim / B || groups * B > lim / nsplit)) return ATTN_E_SHAPE;  // < 2^31
   return ATTN_OK;
 }
@@ -110,11 +112,12 @@ double split_cost(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, in
   const int64_t used = (Lk + len - 1) / len;  // splits with keys
   const int64_t wg = (Hq / Hkv * Lq + p.block_m - 1) / p.block_m * Hkv * B * used;
   const double rounds = std::ceil(static_cast<double>(wg) / slots);
-  double cost = rounds * (static_cast<double>(len) / 32.0 + kOverheadTiles);
+  double cost = rounds * (static_cast<double>(len) / 32.0 * p.tile_cost + kOverheadTiles);
   if (ns > 1) {
-    // One tile of one workgroup: block_m x 32 x D x 4 flop at ~1/slots of ~1.2 PFLOP/s; the
-    // partials are written and read in fp32 and the output written once, at ~4 TB/s.
-    const double tile_s = static_cast<double>(p.block_m) * 32.0 * D * 4.0 / (1.2e15 / slots);
+    // The unit, one key tile of one wide workgroup: 256 x 32 x D x 4 flop at ~1/256 of
+    // ~1.2 PFLOP/s; the partials are written and read in fp32 and the output written once,
+    // at ~4 TB/s.
+    const double tile_s = 256.0 * 32.0 * D * 4.0 / (1.2e15 / kCUs);
     const double bytes = static_cast<double>(B * Hq * Lq) * D * (8.0 * used + 2.0);
     cost += bytes / 4e12 / tile_s + kLaunchTiles;
   }
@@ -137,6 +140,30 @@ int64_t choose_nsplit(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk
   return best;
 }
 
+// The planner's launch: tile shape and key splits.  A key/value group of up to two narrow
+// tiles (129-256 rows) that needs key splits anyway may do better in the narrow shape: with
+// half the rows per workgroup, fewer splits fill the GPU and fewer fp32 partials travel.
+struct Choice {
+  int variant;
+  int64_t nsplit;
+};
+
+Choice choose_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D) {
+  PlanInternal p;
+  plan_for(D, variant_for(Hq, Hkv, Lq), &p);
+  Choice c{p.variant, choose_nsplit(B, Hq, Hkv, Lq, Lk, D, p)};
+  const int64_t rows = Hq / Hkv * Lq;
+  if (c.variant == 0 && c.nsplit > 1 && rows <= 2 * attn_cfg::kNarrowRows) {
+    PlanInternal n;
+    plan_for(D, 1, &n);
+    const int64_t ns = choose_nsplit(B, Hq, Hkv, Lq, Lk, D, n);
+    if (split_cost(B, Hq, Hkv, Lq, Lk, D, ns, n) <
+        0.95 * split_cost(B, Hq, Hkv, Lq, Lk, D, c.nsplit, p))
+      c = Choice{1, ns};
+  }
+  return c;
+}
+
 // attn_fwd_d<D>_<dtype>[_causal][_m128] (_m128: the narrow 128-row shape)
 void kernel_name(int64_t D, int in_dtype, uint32_t flags, int variant, char* out, size_t n) {
   std::snprintf(out, n, "attn_fwd_d%d_%s%s%s", static_cast<int>(D),
@@ -145,14 +172,14 @@ void kernel_name(int64_t D, int in_dtype, uint32_t flags, int variant, char* out
 }
 
 int fill_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
-              int in_dtype, uint32_t flags, int64_t nsplit, attn_plan_t* plan) {
+              int in_dtype, uint32_t flags, int64_t nsplit, int variant, attn_plan_t* plan) {
   PlanInternal p;
-  plan_for_problem(Hq, Hkv, Lq, D, &p);
+  plan_for(D, variant, &p);
   plan->block_m = p.block_m;
   plan->block_n = p.bn;
   plan->waves = p.waves;
   plan->lds_bytes = p.lds;
-  plan->grid = query_tiles(Hq, Hkv, Lq, D) * B * nsplit;
+  plan->grid = query_tiles(Hq, Hkv, Lq, D, variant) * B * nsplit;
   std::memset(plan->kernel, 0, sizeof plan->kernel);
   kernel_name(D, in_dtype, flags, p.variant, plan->kernel, sizeof plan->kernel);
   plan->nsplit = static_cast<int32_t>(nsplit);
@@ -291,7 +318,7 @@ int attn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_
   if (!plan) return ATTN_E_NULLPTR;
   int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype);
   if (rc != ATTN_OK) return rc;
-  return fill_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, 0, 1, plan);
+  return fill_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, 0, 1, variant_for(Hq, Hkv, Lq), plan);
 }
 
 int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
@@ -300,11 +327,14 @@ int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int
   if (flags & ~ATTN_CAUSAL) return ATTN_E_FLAGS;
   int rc = check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype);
   if (rc != ATTN_OK) return rc;
-  PlanInternal p;
-  plan_for_problem(Hq, Hkv, Lq, D, &p);
-  int64_t ns = choose_nsplit(B, Hq, Hkv, Lq, Lk, D, p);
-  while (ns > 1 && check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, ns) != ATTN_OK) --ns;
-  return fill_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, ns, plan);
+  Choice c = choose_plan(B, Hq, Hkv, Lq, Lk, D);
+  int64_t ns = c.nsplit;
+  while (ns > 1 && check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, ns, c.variant) != ATTN_OK) --ns;
+  if (check_shape(B, Hq, Hkv, Lq, Lk, D, in_dtype, ns, c.variant) != ATTN_OK) {
+    c.variant = variant_for(Hq, Hkv, Lq);  // (the default shape's single pass fits: checked)
+    ns = 1;
+  }
+  return fill_plan(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, ns, c.variant, plan);
 }
 
 const char* attn_strerror(int code) {

@@ -170,7 +170,9 @@ int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int
  *              partial results go to the workspace and attn_merge combines them into o and
  *              lse (two launches on `stream`);
  *              0: the planner's choice (attn_plan_ex: more splits when the query tiles
- *              alone would leave compute units idle).
+ *              alone would leave compute units idle; for key/value groups of 129-256 query
+ *              rows that need splits it may also pick the narrow 128-row tile shape, which
+ *              an explicit nsplit never does).
  *   workspace  device memory owned by the caller, 256-byte aligned, at least
  *              attn_workspace_bytes(B, Hq, Lq, D, nsplit) bytes for the nsplit actually
  *              used (query it with attn_plan_ex when passing 0); not retained after the

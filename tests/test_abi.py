@@ -328,18 +328,36 @@ def test_workspace_bytes():
     ((1, 32, 2, 16384, 16384, 256), (1, 1)),    # 2048 workgroups: no split
     ((4, 32, 2, 1024, 16384, 256), (1, 1)),     # 512 workgroups, two full rounds
     ((1, 32, 2, 1024, 16384, 256), (2, 2)),     # 128 workgroups: half the CUs idle unsplit
-    ((1, 32, 2, 16, 16384, 256), (32, 64)),     # decode: 2 workgroups (16 heads x 16 rows each)
+    # decode: 2 wide workgroups unsplit (16 heads x 16 rows each); split, the narrow shape
+    # (two 128-row workgroups per group) needs half as many splits
+    ((1, 32, 2, 16, 16384, 256), (16, 64)),
     ((1, 2, 1, 256, 256, 128), (1, 1)),         # too few keys to split
 ])
 def test_plan_ex_split_choice(shape, expect):
     p = fa.attn_plan_ex(*shape, fa.ATTN_F16, 0)
     assert expect[0] <= p.nsplit <= expect[1], p.nsplit
     base = fa.attn_plan(*shape, fa.ATTN_F16)
-    assert p.grid == base.grid * p.nsplit
     B, Hq, Hkv, Lq, Lk, D = shape
+    # the grid counts the planner's own tiles (its rows per workgroup) and every split
+    assert p.grid == math.ceil(Hq // Hkv * Lq / p.block_m) * Hkv * B * p.nsplit
+    if Hq // Hkv * Lq > 128 and p.block_m == 128:
+        assert p.nsplit > 1 and p.kernel.decode().endswith("_m128")
     assert p.workspace_bytes == fa.attn_workspace_bytes(B, Hq, Lq, D, p.nsplit)
     assert p.split_len == fa.attn_split_range(Lk, p.nsplit, 0)[1]
     assert base.nsplit == 1 and base.workspace_bytes == 0
+
+
+def test_planner_narrow_shape_only_for_split_groups_up_to_256_rows():
+    # 256-row groups that need splits: narrow (with 64 batch entries the narrow shape fills
+    # the GPU with no split at all, rather than the wide one with partials); the same groups
+    # with enough work unsplit, and groups past 256 rows: wide; explicit plans (attn_plan)
+    # keep the default shape
+    assert fa.attn_plan_ex(4, 32, 2, 16, 16384, 256, fa.ATTN_F16, 1).block_m == 128
+    p = fa.attn_plan_ex(64, 32, 2, 16, 4096, 256, fa.ATTN_F16, 0)
+    assert (p.block_m, p.nsplit) == (128, 1)
+    assert fa.attn_plan_ex(256, 32, 2, 16, 4096, 256, fa.ATTN_F16, 0).block_m == 256
+    assert fa.attn_plan_ex(1, 32, 2, 17, 16384, 256, fa.ATTN_F16, 0).block_m == 256
+    assert fa.attn_plan(4, 32, 2, 16, 16384, 256, fa.ATTN_F16).block_m == 256
 
 
 def test_plan_ex_names_the_causal_kernel():
