@@ -57,7 +57,9 @@
  *
  * Ownership.  Every pointer is device memory owned by the caller (for
  * example torch tensors).  The library never allocates, frees, retains or
- * synchronises; it keeps no mutable global state and is reentrant.
+ * synchronises, and is reentrant: its only mutable global state is one bit
+ * per device and kernel recording that the kernel's LDS limit was raised
+ * (hipFuncSetAttribute, set once on first use, updated atomically).
  *
  * Errors.  Arguments are validated on the host before anything is
  * launched; a negative return means nothing was enqueued and nothing
