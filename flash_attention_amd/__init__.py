@@ -26,8 +26,8 @@ ATTN_MAX_SPLITS = 256
 ATTN_OK = 0
 ERROR_CODES = {
     -1: "ATTN_E_NULLPTR", -2: "ATTN_E_SHAPE", -3: "ATTN_E_HEADDIM", -4: "ATTN_E_GQA",
-    -5: "ATTN_E_DTYPE", -6: "ATTN_E_SCALE", -7: "ATTN_E_ALIGN", -8: "ATTN_E_ALIAS",
-    -9: "ATTN_E_LAUNCH", -10: "ATTN_E_FLAGS", -11: "ATTN_E_SPLIT", -12: "ATTN_E_WORKSPACE",
+    -5: "ATTN_E_DTYPE", -6: "ATTN_E_SCALE", -7: "ATTN_E_ALIGN", -8: "ATTN_E_LAUNCH",
+    -9: "ATTN_E_ALIAS", -10: "ATTN_E_FLAGS", -11: "ATTN_E_SPLIT", -12: "ATTN_E_WORKSPACE",
 }
 
 _I64 = ctypes.c_int64

@@ -5,9 +5,9 @@
 
 #include "../../include/attn.h"
 
-// Dense fp16/bf16 matrix-core peak: every compute unit retires one
-// v_mfma_f32_32x32x16_{f16,bf16} (2*32*32*16 = 32768 flop) per 8 clocks on each of its four
-// SIMDs, i.e. 4096 flop per clock per compute unit.
+// Dense fp16/bf16 matrix-core peak: each of a compute unit's four SIMDs retires one
+// v_mfma_f32_32x32x16_{f16,bf16} (2*32*32*16 = 32768 flop) per 8 passes of 4 clocks
+// (32 clocks), i.e. 1024 flop per clock per SIMD and 4096 per compute unit.
 extern "C" int attn_device_peak(double* tflops, int32_t* compute_units, int32_t* clock_khz) {
   int dev = 0, cus = 0, khz = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

@@ -98,9 +98,10 @@ enum {
   ATTN_E_DTYPE = -5,   /* in_dtype is neither ATTN_F16 nor ATTN_BF16 */
   ATTN_E_SCALE = -6,   /* scale is NaN or infinite */
   ATTN_E_ALIGN = -7,   /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
-  ATTN_E_ALIAS = -8,   /* o or lse overlaps an input, or lse overlaps o */
-  ATTN_E_LAUNCH = -9,  /* the HIP runtime refused the launch (stream in an error state,
+  ATTN_E_LAUNCH = -8,  /* the HIP runtime refused the launch (stream in an error state,
                           invalid stream, no device) */
+  /* codes past the first eight: checks of the options and of the extra entry points */
+  ATTN_E_ALIAS = -9,   /* o or lse overlaps an input, or lse overlaps o */
   ATTN_E_FLAGS = -10,  /* a flag bit other than ATTN_CAUSAL is set */
   ATTN_E_SPLIT = -11,  /* nsplit outside 0..ATTN_MAX_SPLITS (1..ATTN_MAX_SPLITS where a
                           count is required), or a split index out of range */
@@ -110,6 +111,10 @@ enum {
 
 /*
  * attn_fwd -- enqueue the attention forward pass on the null stream.
+ * Defines: the operation at the top of this file, as the "Xe2 ... ESIMD Flash Attention --
+ * HD=256" page states it (header: GQA, 32 query over 2 KV heads, HD=256) with the data flow
+ * of "Xe2 Sdp Bf16", section "Kernel Architecture: bf16io" (scores, fp32 softmax, weighted
+ * V, one reciprocal of the row sum, 16-bit output).
  *   q        [B,Hq,Lq,D] input, element type in_dtype
  *   k, v     [B,Hkv,Lk,D] inputs, element type in_dtype
  *   o        [B,Hq,Lq,D] output, element type in_dtype (must not overlap q, k, v)
@@ -122,18 +127,23 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int in_dtype);
 
 /* attn_fwd on an explicit stream: `stream` is a hipStream_t passed as void* (NULL = null
- * stream), e.g. torch.cuda.current_stream().cuda_stream. */
+ * stream), e.g. torch.cuda.current_stream().cuda_stream.  Same operation and passages as
+ * attn_fwd; arguments, ownership and errors as there. */
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse,
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                     float scale, int in_dtype, void* stream);
 
 /* The host-side argument check attn_fwd runs before any launch.  Pure CPU, no HIP call:
- * usable without a GPU.  Returns ATTN_OK or the code attn_fwd would return. */
+ * usable without a GPU.  Returns ATTN_OK or the code attn_fwd would return.  Unsupported
+ * shapes are refused on the host before any dispatch, the way the generic ESIMD GEMM of
+ * "XPU 算子开发最佳实践：GEMM 高性能优化指南" (section 四) checks its shape before choosing a
+ * compiled template. */
 int attn_validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                   float scale, int in_dtype);
 
-/* Static text for a return code (never NULL). */
+/* Static text for a return code (never NULL); the codes are those of the host-side checks
+ * above (same GEMM-guide passage, section 四). */
 const char* attn_strerror(int code);
 
 /* The launch the planner picks for a problem: tile sizes, waves per workgroup, LDS bytes
@@ -153,19 +163,26 @@ typedef struct {
 
 /* Fill *plan for the given problem without launching anything (pure CPU): the launch of
  * attn_fwd (never split).  Returns ATTN_OK or the validation code for the shape/dtype
- * arguments. */
+ * arguments.  A tiling chosen per head dimension, as the "Xe2 ... ESIMD Flash Attention --
+ * HD=256" page fixes its own per head dimension (sections "Kernel Constants" and "HD=256
+ * Architecture Differences (vs HD=128)"). */
 int attn_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
               int in_dtype, attn_plan_t* plan);
 
 /* The launch attn_fwd_ex makes with nsplit = 0 and these flags: the planner picks the number
  * of key splits from a cost model of the GPU's 256 compute units (one or two workgroups each,
- * by tile shape), the
- * key range per workgroup and the merge traffic. */
+ * by tile shape), the key range per workgroup and the merge traffic.  Shape- and
+ * batch-dependent dispatch of the attention launch: SyclKittens summary, section E.5;
+ * split-K: section E.2.  Pure CPU; returns ATTN_OK or a validation code. */
 int attn_plan_ex(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
                  int in_dtype, uint32_t flags, attn_plan_t* plan);
 
 /*
  * attn_fwd_ex -- attn_fwd with options, on an explicit stream.
+ * Defines: attn_fwd's operation, optionally under the causal mask (SyclKittens summary,
+ * sections B.1.2, E.4, E.6; diagonal as stated at the top of this file) and computed over
+ * key splits whose partial results are merged (split-K: section E.2; merge of online-
+ * softmax state: section I.2).
  *   flags      0 or ATTN_CAUSAL
  *   nsplit     1: one pass, as attn_fwd (workspace unused, may be NULL);
  *              2..ATTN_MAX_SPLITS: the keys are cut into nsplit ranges (attn_split_range),
@@ -187,13 +204,18 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int in_dtype, uint32_t flags, int64_t nsplit, void* workspace,
                 int64_t workspace_bytes, void* stream);
 
-/* attn_validate for attn_fwd_ex's arguments other than the workspace (pure CPU). */
+/* attn_validate for attn_fwd_ex's arguments other than the workspace (pure CPU); host-side
+ * refusal before dispatch as for attn_validate (GEMM guide, section 四).  Returns ATTN_OK or
+ * the code attn_fwd_ex would return for these arguments. */
 int attn_validate_ex(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
                      int64_t D, float scale, int in_dtype, uint32_t flags, int64_t nsplit);
 
 /*
  * attn_fwd_partial -- partial results over key ranges, one launch.
+ * Defines: the per-range online-softmax state (normalised output and log-sum-exp of each
+ * row over one key range) that the SyclKittens summary, section I.2, merges across key
+ * shards, and that its split-K (section E.2) computes per workgroup.
  *   o_part    [nsplit, B, Hq, Lq, D] fp32 output: split s holds each row's attention over
  *             the keys of attn_split_range(Lk, nsplit, s) alone (0 for a row that sees none)
  *   lse_part  [nsplit, B, Hq, Lq] fp32 output: that range's natural-log sum of
@@ -207,7 +229,8 @@ int attn_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
                      int64_t Lk, int64_t D, float scale, int in_dtype, uint32_t flags,
                      int64_t nsplit, void* stream);
 
-/* attn_fwd_partial's argument check (pure CPU). */
+/* attn_fwd_partial's argument check (pure CPU; GEMM guide, section 四, as attn_validate).
+ * Returns ATTN_OK or the code attn_fwd_partial would return. */
 int attn_validate_partial(const void* q, const void* k, const void* v, const float* o_part,
                           const float* lse_part, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
                           int64_t Lk, int64_t D, float scale, int in_dtype, uint32_t flags,
@@ -215,6 +238,8 @@ int attn_validate_partial(const void* q, const void* k, const void* v, const flo
 
 /*
  * attn_merge -- combine nsplit partial results per row into the full result.
+ * Defines: the merge of online-softmax state of the SyclKittens summary, section I.2
+ * (LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s, as at the top of this file).
  *   o_part    [nsplit, rows, D] fp32;  lse_part [nsplit, rows] fp32 (natural log, -inf for
  *             an empty part)
  *   o         [rows, D] output of element type out_dtype (ATTN_F16, ATTN_BF16, ATTN_F32),
@@ -230,28 +255,31 @@ int attn_validate_partial(const void* q, const void* k, const void* v, const flo
 int attn_merge(const float* o_part, const float* lse_part, int64_t nsplit, int64_t rows,
                int64_t D, void* o, float* lse, int out_dtype, void* stream);
 
-/* attn_merge's argument check (pure CPU). */
+/* attn_merge's argument check (pure CPU; GEMM guide, section 四, as attn_validate).
+ * Returns ATTN_OK or the code attn_merge would return. */
 int attn_validate_merge(const float* o_part, const float* lse_part, int64_t nsplit,
                         int64_t rows, int64_t D, const void* o, const float* lse,
                         int out_dtype);
 
 /* Key range [*begin, *end) of split s (0 <= s < nsplit) of Lk >= 0 keys: ranges of
  * ceil(ceil(Lk / nsplit) / 64) * 64 keys from key 0, the last ones cut at Lk or empty
- * (begin = end = Lk).  Pure CPU.  Returns ATTN_OK, ATTN_E_SHAPE or ATTN_E_SPLIT. */
+ * (begin = end = Lk).  Pure CPU.  Returns ATTN_OK, ATTN_E_NULLPTR, ATTN_E_SHAPE or
+ * ATTN_E_SPLIT.  The key ranges of split-K (SyclKittens summary, section E.2). */
 int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int64_t* end);
 
 /* Workspace bytes attn_fwd_ex needs for nsplit splits (0 for nsplit = 1 or no query row),
  * or a negative code for bad sizes.  Layout: O_part at offset 0, LSE_part at the next
- * 256-byte boundary. */
+ * 256-byte boundary: the per-split state of split-K (SyclKittens summary, section E.2). */
 int64_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t nsplit);
 
 /* Dense fp16/bf16 MFMA peak of the current HIP device: compute units x peak shader clock x
  * 4096 flop per clock per compute unit (the gfx950 rate of v_mfma_f32_32x32x16_{f16,bf16}).
  * Any pointer may be NULL.  Returns ATTN_OK, or ATTN_E_LAUNCH if the HIP runtime reports no
- * device. */
+ * device.  The denominator of "% of peak", as the "Xe2 ... ESIMD Flash Attention -- HD=256"
+ * page reports its result (header: TFLOPS and percent of the device's peak). */
 int attn_device_peak(double* tflops, int32_t* compute_units, int32_t* clock_khz);
 
-/* Library version, "major.minor.patch". */
+/* Library version, "major.minor.patch" (static string; not a computation of the pages). */
 const char* attn_version(void);
 
 #ifdef __cplusplus

@@ -92,8 +92,8 @@ def test_validate_accepts_good_arguments():
     (dict(scale=math.inf), -6), (dict(scale=math.nan), -6), (dict(scale=-math.inf), -6),
     (dict(q=Q + 8), -7), (dict(k=K + 2), -7), (dict(v=V + 4), -7), (dict(o=O + 1), -7),
     (dict(lse=L + 2), -7),
-    (dict(o=Q), -8), (dict(o=K + 4096), -8), (dict(o=V), -8), (dict(lse=O + 256), -8),
-    (dict(lse=Q), -8), (dict(lse=K), -8),
+    (dict(o=Q), -9), (dict(o=K + 4096), -9), (dict(o=V), -9), (dict(lse=O + 256), -9),
+    (dict(lse=Q), -9), (dict(lse=K), -9),
 ])
 def test_validate_rejects(over, code):
     assert validate(**over) == code
@@ -197,7 +197,7 @@ def test_binding_output_check():
 def test_lse_may_follow_o_directly():
     qbytes = 1 * 32 * 4096 * 256 * 2
     assert validate(lse=O + qbytes) == 0
-    assert validate(lse=O + qbytes - 4) == -8
+    assert validate(lse=O + qbytes - 4) == -9
 
 
 @pytest.mark.parametrize("D,dtype", [(128, fa.ATTN_F16), (128, fa.ATTN_BF16),
@@ -238,7 +238,7 @@ def test_validate_ex():
     assert validate_ex(flags=2) == -10 and validate_ex(flags=0x80000000) == -10
     assert validate_ex(nsplit=-1) == -11 and validate_ex(nsplit=fa.ATTN_MAX_SPLITS + 1) == -11
     # the plain checks still run
-    assert validate_ex(flags=fa.ATTN_CAUSAL, D=64) == -3 and validate_ex(o=Q) == -8
+    assert validate_ex(flags=fa.ATTN_CAUSAL, D=64) == -3 and validate_ex(o=Q) == -9
     # Lq > Lk is allowed under the causal mask (early rows are empty)
     assert validate_ex(flags=fa.ATTN_CAUSAL, Lq=5000, Lk=100) == 0
 
@@ -260,11 +260,11 @@ def test_validate_partial():
     assert validate_partial(nsplit=0) == -11 and validate_partial(nsplit=257) == -11
     assert validate_partial(flags=4) == -10
     assert validate_partial(o_part=P_O + 4) == -7 and validate_partial(lse_part=P_L + 2) == -7
-    assert validate_partial(o_part=Q) == -8 and validate_partial(lse_part=K) == -8
+    assert validate_partial(o_part=Q) == -9 and validate_partial(lse_part=K) == -9
     # o_part of 4 splits: 4 * 32 * 4096 * 256 * 4 bytes = 0.5 GiB; lse_part just after is fine
     pbytes = 4 * 32 * 4096 * 256 * 4
     assert validate_partial(lse_part=P_O + pbytes) == 0
-    assert validate_partial(lse_part=P_O + pbytes - 4) == -8
+    assert validate_partial(lse_part=P_O + pbytes - 4) == -9
     assert validate_partial(D=100) == -3 and validate_partial(Hkv=5) == -4
 
 
@@ -288,8 +288,8 @@ def test_validate_merge():
     assert validate_merge(out_dtype=3) == -5 and validate_merge(out_dtype=-1) == -5
     assert validate_merge(o=O + 8) == -7 and validate_merge(lse=L + 1) == -7
     assert validate_merge(o_part=P_O + 4) == -7
-    assert validate_merge(o=P_O) == -8 and validate_merge(lse=P_L) == -8
-    assert validate_merge(lse=O + 4) == -8
+    assert validate_merge(o=P_O) == -9 and validate_merge(lse=P_L) == -9
+    assert validate_merge(lse=O + 4) == -9
 
 
 @pytest.mark.parametrize("Lk,nsplit", [(1, 1), (1, 5), (63, 2), (64, 2), (1000, 3),
@@ -397,7 +397,7 @@ def test_merge_and_partial_reject_before_any_launch():
     assert fa.attn_merge(P_O, P_L, 0, 10, 128, O, L, fa.ATTN_F16, None) == -11
     assert fa.attn_merge(P_O, P_L, 2, 10, 100, O, L, fa.ATTN_F16, None) == -3
     assert fa.attn_merge(P_O, None, 2, 10, 128, O, L, fa.ATTN_F16, None) == -1
-    assert fa.attn_merge(P_O, P_L, 2, 10, 128, P_O, L, fa.ATTN_F16, None) == -8
+    assert fa.attn_merge(P_O, P_L, 2, 10, 128, P_O, L, fa.ATTN_F16, None) == -9
     a = GOOD
     assert fa.attn_fwd_partial(a["q"], a["k"], a["v"], P_O, None, a["B"], a["Hq"], a["Hkv"],
                                a["Lq"], a["Lk"], a["D"], a["scale"], a["in_dtype"], 0, 2,
