@@ -81,6 +81,14 @@ WORKLOADS = {
                                   seed_base=8000, causal=True, nsplit=0),
     "decode1x64k_d128_bf16": Workload("decode1x64k_d128_bf16", 1, 32, 8, 1, 65536, 128,
                                       "bf16", seed_base=9000, causal=True, nsplit=0),
+    # The headline shape over sharper score ranges ("multiple data ranges" of the HD=256
+    # page's section "Performance Testing"): K scaled by 4 and by 8 before the rounding to
+    # fp16, so that later key tiles outgrow a row's first-tile maximum and the kernel's lazy
+    # rescale runs (scores ~ N(0, 16) and N(0, 64) in natural-log units).
+    "gqa16k_d256_k4": Workload("gqa16k_d256_k4", 1, 32, 2, 16384, 16384, 256, "f16",
+                               k_mult=4.0, seed_base=10000),
+    "gqa16k_d256_k8": Workload("gqa16k_d256_k8", 1, 32, 2, 16384, 16384, 256, "f16",
+                               k_mult=8.0, seed_base=11000),
 }
 HEADLINE = "gqa16k_d256"
 

@@ -18,8 +18,12 @@ SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_merge.hi
            os.path.join(CSRC, "attn_device.hip"), os.path.join(CSRC, "attn_host.cpp")]
 
 # Packed fp32 VALU instructions are kept out of the device code: the compiler would
-# otherwise form them from ordinary float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# otherwise form them from ordinary float code.  The key loop's `#pragma unroll` loops must
+# unroll completely (their arrays are indexed by the loop counters, and a loop left rolled
+# would move those arrays to scratch memory); the default size limit for forced unrolling is
+# below the attention kernel's loop bodies, so it is raised.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-pragma-unroll-threshold=1000000"]
 
 
 def build(out=LIB, extra=(), quiet=False, save_temps_dir=None):

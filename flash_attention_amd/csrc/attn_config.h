@@ -77,8 +77,7 @@ constexpr int waves_per_simd() { return Tile<D, V>::WAVES * Tile<D, V>::WG_PER_C
 // Query rows per key/value group up to which the narrow shape is used.
 constexpr int kNarrowRows = 128;
 
-// STAGES x (K tile + V tile), each [BN][D] 16-bit elements, plus the restart flag (16
-// bytes reserved).
-constexpr int lds_bytes(int d, int bn, int stages) { return stages * 2 * bn * d * 2 + 16; }
+// STAGES x (K tile + V tile), each [BN][D] 16-bit elements.
+constexpr int lds_bytes(int d, int bn, int stages) { return stages * 2 * bn * d * 2; }
 
 }  // namespace attn_cfg

@@ -22,8 +22,9 @@
 // (32 keys x 16 dims) and Q^T as the B operand (16 dims x 32 queries, register resident
 // for the whole key loop).  The 32x32 fp32 result then holds one query per lane column:
 // lane l owns query l%32 and 16 of the 32 keys, the other 16 sitting in lane l^32.  Row
-// max = an in-lane max plus one cross-half exchange (needed for the first tile only: its
-// maximum is the reference for the whole sweep); the row sum stays per-lane until the end.
+// max = an in-lane max plus one cross-half exchange (needed for the first tile, whose
+// maximum is the row's softmax reference, and for the rare tile whose scores outgrow it);
+// the row sum stays per-lane until the end.
 // Those same registers, rounded to 16 bits, are directly the B operand of
 // O^T += V^T * P^T (k index = key): no trip through LDS for P.  The key order inside the
 // B operand is fixed by the accumulator layout, so V^T must be read in that same
@@ -229,11 +230,15 @@ __device__ __forceinline__ void lds_dma16_so(i32x4 rsrc, uint32_t voffset, uint3
                : "memory");
 }
 
-// Growth threshold.  The exponentials use a per-row reference m fixed by the first key tile;
-// as long as no lane's partial sum over a tile exceeds 2^15, no weight does either, and fp16
-// (largest value 65504) holds every weight.  Exact in real arithmetic: numerator and
-// denominator share m.
-constexpr float kGrowth = 32768.0f;
+// Growth threshold of the lazy rescale.  The exponentials use a per-row reference m: the
+// first key tile's maximum, raised only when a later tile outgrows it by this factor.  All
+// weights are non-negative, so a lane whose partial sum over a tile stays at or below the
+// threshold has no weight above it.  fp16 weights must stay below 65504: the fp16 kernel
+// rescales past 2^15.  bf16 weights have fp32's range, and the bf16 kernel waits until 2^24
+// (row sums and the fp32 accumulator stay far from overflow).  Exact in real arithmetic for
+// any m: numerator and denominator share it.
+template <typename T>
+constexpr float kGrowth = std::is_same<T, _Float16>::value ? 32768.0f : 16777216.0f;
 
 // V selects the tile shape (attn_config.h): 0 wide, 1 narrow.  The second launch bound is
 // the number of wavefronts that share a SIMD, which caps the registers of one wavefront.
@@ -264,10 +269,6 @@ void attn_fwd_kernel(Params p) {
 
   extern __shared__ u32x4 smem_raw[];
   uint16_t* const smem = reinterpret_cast<uint16_t*>(smem_raw);
-  // The restart flag after the K/V stages (written by at most one lane per wave), read
-  // through an LDS pointer so the read waits on LDS traffic only.
-  typedef __attribute__((address_space(3))) volatile int lds_vint;
-  lds_vint* const restart_flag = (lds_vint*)(smem + NSTAGE * 2 * TILE);
   // LDS byte address of the stages, for the copy destinations (M0).
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)smem));
 
@@ -428,7 +429,6 @@ void attn_fwd_kernel(Params p) {
 
   if (ntiles > 0) issue_tile(0, 0);
   if (ntiles > 1) issue_tile(1, 1);
-  if (tid == 0) restart_flag[0] = 0;
 
   // ---- per-lane LDS byte offsets of the fragment reads (stage base added later) ----
   // K (A operand of S^T): row l%32, chunk 2kk+hi at slot (2kk+hi) ^ sw, sw = swz_k(l%32);
@@ -578,8 +578,7 @@ void attn_fwd_kernel(Params p) {
     mt[qb] = x * c;  // this tile's maximum of scale*log2(e)*score for the row
     pin(mt[qb]);
   };
-  // The first tile fixes the reference: m = its row maximum (or the exact maximum found
-  // by a restart's maximum sweep, which is never smaller).
+  // The first tile fixes the reference: m = its row maximum.
   auto set_reference = [&]() {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m[qb] = fmaxf(m[qb], mt[qb]);
@@ -606,17 +605,53 @@ void attn_fwd_kernel(Params p) {
       }
     }
   };
-  // Growth check of tile t >= 1, after its exponentials: a weight above kGrowth (the scores
-  // outgrew the reference) shows up as a lane's partial tile sum above kGrowth, since all
-  // weights are non-negative.  The wave remembers it; the workgroup looks once, at the end
-  // of the sweep.  After a restart m holds the exact maxima (no weight exceeds 1) and the
-  // check is off, so a sweep restarts at most once whatever the data.
-  bool exact_m = false, grew = false;
-  auto check_growth = [&]() {
-    bool grow = false;
+  // Lazy rescale after the exponentials of a tile t >= 1: the deferred compensation of the
+  // online softmax ("Key Optimization Insights / What Worked" of the HD=256 page), done
+  // only where a tile's scores outgrow the reference.  A lane whose partial sum of the
+  // tile's weights exceeds kGrowth holds a weight above it (weights are non-negative).  If
+  // any lane of the wave does, the wave raises each row's reference to the tile's maximum
+  // where that is larger, m' = max(m, mt), multiplies the row's output accumulator and
+  // sum by exp2(m - m') <= 1, and recomputes the tile's weights against m' (now at most
+  // 1).  The accumulator then holds tiles 0..t-1 against m', as the P.V product of tile t
+  // expects.  The scores themselves are not kept for this rare case (32 registers the wide
+  // HD=256 shape does not have): they are computed again from K(t), which stays in its LDS
+  // stage until tile t+4 is copied.  Each wave decides for its own rows; no other wave
+  // waits beyond the next barrier.
+  auto rescale_if_grown = [&](const char* ks, int t, u32x4 (&pcur)[QB][2]) {
+    bool grown[QB], any = false;  // per query block, wave-uniform
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) grow |= lt[qb] > kGrowth;
-    grew |= __builtin_amdgcn_ballot_w64(grow) != 0;  // wave-uniform
+    for (int qb = 0; qb < QB; ++qb) {
+      grown[qb] = __builtin_amdgcn_ballot_w64(lt[qb] > kGrowth<T>) != 0;
+      any |= grown[qb];
+    }
+    if (!any) return;
+    f32x16 s2[QB];
+    u32x4 kf2[3];
+    kf2[0] = kfrag(ks, 0);
+    kf2[1] = kfrag(ks, 1);
+    qk(ks, s2, kf2, [] {});
+    mfma_fence_v(s2);
+    mask_keys(s2, t);
+    attn_agpr::fence();  // the last P.V MFMA's results have landed
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (!grown[qb]) continue;  // that block's rows keep their reference
+      row_max(s2, qb);
+      const float mn = fmaxf(m[qb], mt[qb]);
+      const float delta = __builtin_amdgcn_exp2f(m[qb] - mn);
+      m[qb] = mn;
+      l[qb] *= delta;
+      // this block's weights and partial sums against m', a pair at a time (the scheduling
+      // barriers keep the compiler from computing all of them before packing any)
+#pragma unroll
+      for (int e = 16 * qb; e < 16 * qb + 16; e += 2) {
+        exp_slice(s2, pcur, e, e + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) attn_agpr::scale(qb * DB + db, delta);
+    }
+    attn_agpr::fence_write();
   };
 
   // Synchronisation point of iteration t (near the end of its P.V steps): tile t+1 has
@@ -691,9 +726,9 @@ void attn_fwd_kernel(Params p) {
         if (hb == QB - 1 && s >= SYNC_STEP && t + 2 < ntiles && wv / COPY_WAVES == s - SYNC_STEP)
           issue_tile(t + 2, (ST + 2) % NSTAGE);
         if (h == H - 1) {
+          if constexpr (PV) rescale_if_grown(kstage(ST), t, pcur);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
-          if (PV && !exact_m) check_growth();
           if (t + 1 < ntiles) {
             // first two K fragments of tile t+1 (landed at the sync point)
             kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
@@ -719,48 +754,17 @@ void attn_fwd_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Exact row maxima over all key tiles (S^T products only), for a restart: afterwards no
-  // weight exceeds 1 and no tile can trigger another restart.  Uses the same stages and
-  // copies as the main sweep; every stage is idle on entry and on exit.
-  auto max_sweep = [&]() {
-    issue_tile(0, 0);
-    if (ntiles > 1) issue_tile(1, 1);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) m[qb] = kWorst * c;  // -inf in scaled units
-    for (int t = 0; t < ntiles; ++t) {
-      if (t + 1 < ntiles) WAIT_VMCNT(2 * LOADS);  // tile t landed (tile t+1 may not have)
-      else WAIT_VMCNT(0);
-      __syncthreads();  // tile t visible; every wave is done with tile t-2's stage
-      if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % NSTAGE);
-      kf[0] = kfrag(kstage(t % NSTAGE), 0);
-      kf[1] = kfrag(kstage(t % NSTAGE), 1);
-      f32x16 sacc[QB];
-      qk(kstage(t % NSTAGE), sacc, kf, [] {});
-      mfma_fence_v(sacc);
-      mask_keys(sacc, t);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) row_max(sacc, qb);
-      set_reference();
-    }
-    finite_reference();
-    WAIT_VMCNT(0);
-    __syncthreads();  // nobody reads a stage any more
-  };
-
   // ---- the key loop ----
-  // The weights use a per-row reference m fixed by the first key tile instead of the usual
-  // running maximum, so the output accumulator is never rescaled (it is only ever written
-  // by MFMAs).  If a later tile outgrows m by more than a factor kGrowth (rare: the scores
-  // must grow by 15 in log2 units), the sweep's results are discarded: a maximum sweep finds
-  // the exact row maxima and the key sweep starts over with zeroed accumulators.  Exact in
-  // real arithmetic for any m: numerator and denominator share it.  The loop is unrolled by
-  // four: the stage of each iteration is a compile-time constant and the two P buffers
-  // swap roles without copies.
+  // The weights use a per-row reference m set by the first key tile instead of a maximum
+  // kept up to date at every tile, so the output accumulator is rescaled only in the rare
+  // tile whose scores outgrow m by more than a factor kGrowth (rescale_if_grown).  The loop
+  // is unrolled by four: the stage of each iteration is a compile-time constant and the two
+  // P buffers swap roles without copies.
   u32x4 pa[QB][2], pb2[QB][2];
   f32x16 sacc[QB];  // scores of the current tile
   // (a workgroup with no key to look at, under the causal mask or past the last split,
   // skips the loop: its rows are empty)
-  if (ntiles > 0) for (;;) {
+  if (ntiles > 0) {
     if (ntiles > 1) WAIT_VMCNT(2 * LOADS);  // tile 0 landed (tile 1 may be in flight)
     else WAIT_VMCNT(0);
     __syncthreads();
@@ -782,32 +786,8 @@ void attn_fwd_kernel(Params p) {
       iteration(std::true_type{}, S0{}, t, pb2, pa, sacc);
       ++t;
     }
-    // Did any wave see its scores outgrow the reference?  (The writer waits for its flag
-    // before the barrier; every wave reads it before the next barrier.)
-    if (grew) {
-      if (lane == 0) restart_flag[0] = 1;
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    }
-    __builtin_amdgcn_s_barrier();
-    if (__builtin_amdgcn_readfirstlane(restart_flag[0]) == 0) {
-      if (ntiles & 1) drain(ntiles - 1, pa);  // P(t) lives in pa for even t
-      else drain(ntiles - 1, pb2);
-      break;
-    }
-    WAIT_VMCNT(0);
-    __syncthreads();  // nobody still reads a stage or the flag
-    if (tid == 0) restart_flag[0] = 0;  // (ordered by the barriers of the maximum sweep)
-    max_sweep();
-    exact_m = true;  // no further growth checks: no wave can set grew again
-    grew = false;
-    issue_tile(0, 0);
-    if (ntiles > 1) issue_tile(1, 1);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      l[qb] = 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) attn_agpr::zero(qb * DB + db);
-    }
+    if (ntiles & 1) drain(ntiles - 1, pa);  // P(t) lives in pa for even t
+    else drain(ntiles - 1, pb2);
   }
 
   // Epilogue: O = O^T / l (one reciprocal per row), LSE = ln2 * (m + log2 l).  An empty

@@ -14,6 +14,8 @@ import subprocess
 
 import pytest
 
+from flash_attention_amd import build as lib_build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "flash_attention_amd", "csrc")
 SOURCES = [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "attn_merge.hip")]
@@ -25,8 +27,8 @@ def asm(tmp_path_factory):
     for src in SOURCES:
         out = str(tmp_path_factory.mktemp("asm") / (os.path.basename(src) + ".s"))
         cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17",
-               "-I" + os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang",
-               "-packed-fp32-ops", "--cuda-device-only", "-S", src, "-o", out]
+               "-I" + os.path.join(ROOT, "include"), *lib_build.DEVICE_FLAGS,
+               "--cuda-device-only", "-S", src, "-o", out]
         subprocess.run(cmd, check=True, capture_output=True)
         text.append(open(out).read())
     return "\n".join(text)

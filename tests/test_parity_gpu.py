@@ -282,8 +282,8 @@ def _growing_scores(D, dt, Lk, spikes, seed):
 
 @pytest.mark.parametrize("D,dt", [(256, "f16"), (128, "bf16"), (256, "bf16")])
 def test_reference_growth_mid_sweep(D, dt):
-    """A score far above the first tile's maximum in a later tile (forces the kernel to
-    restart its key sweep with a higher reference)."""
+    """A score far above the first tile's maximum in a later tile (the wave holding the row
+    rescales its accumulator and sums to a higher reference)."""
     _announce("growth mid sweep D=%d %s" % (D, dt))
     q, k, v = _growing_scores(D, dt, 700, [(333, 300.0)], seed=21)
     parity(q, k, v, scale_of(D), dt, what="growth mid")
@@ -303,9 +303,9 @@ def test_reference_growth_last_tile_and_repeated():
 @pytest.mark.parametrize("D,dt", [(128, "f16"), (128, "bf16"), (256, "f16")])
 @pytest.mark.parametrize("causal,nsplit", [(False, 3), (True, 1), (True, 2)])
 def test_reference_growth_with_mask_and_splits(D, dt, causal, nsplit):
-    """Scores outgrowing the first tile's maximum, in several tiles (a restart of the key
-    sweep), under the causal mask and inside key splits (each split has its own first tile
-    and its own restart)."""
+    """Scores outgrowing the first tile's maximum, in several tiles (a rescale each time),
+    under the causal mask and inside key splits (each split has its own first tile and its
+    own reference)."""
     _announce("growth D=%d %s causal=%s nsplit=%d" % (D, dt, causal, nsplit))
     q, k, v = _growing_scores(D, dt, 900, [(130, 200.0), (480, 350.0), (899, 500.0)],
                               seed=24 + nsplit)
