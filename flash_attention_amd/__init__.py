@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 ATTN_F16, ATTN_BF16, ATTN_F32 = 0, 1, 2
 ATTN_CAUSAL = 1
 ATTN_MAX_SPLITS = 256
+ATTN_NOALLOC_WORKSPACE_BYTES = 64 << 20
 ATTN_OK = 0
 ERROR_CODES = {
     -1: "ATTN_E_NULLPTR", -2: "ATTN_E_SHAPE", -3: "ATTN_E_HEADDIM", -4: "ATTN_E_GQA",
@@ -91,6 +92,8 @@ def lib():
         L.attn_workspace_bytes.restype = _I64
         L.attn_plan_ex.argtypes = shape + [ctypes.c_int, U32, ctypes.POINTER(AttnPlan)]
         L.attn_plan_ex.restype = ctypes.c_int
+        L.attn_fwd_ex_noalloc.argtypes = L.attn_fwd.argtypes + [U32, _I64, _VP]
+        L.attn_fwd_ex_noalloc.restype = ctypes.c_int
         L.attn_device_peak.argtypes = [ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int32),
                                        ctypes.POINTER(ctypes.c_int32)]
@@ -135,6 +138,12 @@ def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, flags, 
                 workspace, workspace_bytes, stream):
     return lib().attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, flags,
                              nsplit, workspace, workspace_bytes, stream)
+
+
+def attn_fwd_ex_noalloc(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, flags,
+                        nsplit, stream):
+    return lib().attn_fwd_ex_noalloc(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype,
+                                     flags, nsplit, stream)
 
 
 def attn_validate_ex(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, flags, nsplit):

@@ -954,6 +954,36 @@ int launch_attn(const Params& prm, int64_t D, int in_dtype, int block_m, int64_t
 
 }  // namespace
 
+// The library's own workspace for attn_fwd_ex_noalloc, the entry point for callers that
+// cannot allocate: one copy of this array on every GPU the library runs on, held until the
+// process ends.  In host code `scratch` is a host-side stand-in, not a device address; the
+// device address of each GPU's copy comes from hipGetSymbolAddress, is kept in
+// scratch_addr below, and is the only form in which the array reaches a kernel.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first call made with
+// that device current; nullptr if the HIP runtime cannot say (no device, or past the 64th).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  uintptr_t a = scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    a = reinterpret_cast<uintptr_t>(ptr);
+    scratch_addr[dev].store(a, std::memory_order_release);  // (a racing caller stores the same)
+  }
+  return reinterpret_cast<void*>(a);
+}
+
+}  // namespace
+
 extern "C" {
 
 int attn_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -1038,6 +1068,35 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   rc = launch_attn(prm, D, in_dtype, plan.block_m, plan.grid, s);
   if (rc != ATTN_OK) return rc;
   return attn_merge(o_part, lse_part, nsplit, rows, D, o, lse, in_dtype, stream);
+}
+
+int attn_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                        float scale, int in_dtype, uint32_t flags, int64_t nsplit,
+                        void* stream) {
+  const int rc = attn_validate_ex(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype,
+                                  flags, nsplit);
+  if (rc != ATTN_OK) return rc;
+  if (B * Hq * Lq == 0) return ATTN_OK;
+  const int64_t cap = ATTN_NOALLOC_WORKSPACE_BYTES;
+  if (nsplit == 0) {
+    // the planner's launch if its partials fit; otherwise the most splits that fit (default
+    // tile shape), down to one pass, which needs no workspace
+    attn_plan_t plan;
+    const int prc = attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, in_dtype, flags, &plan);
+    if (prc != ATTN_OK) return prc;
+    if (plan.workspace_bytes > cap) {
+      int64_t ns = plan.nsplit;
+      while (ns > 1 && attn_workspace_bytes(B, Hq, Lq, D, ns) > cap) --ns;
+      nsplit = ns;
+    }
+  } else if (attn_workspace_bytes(B, Hq, Lq, D, nsplit) > cap) {
+    return ATTN_E_WORKSPACE;
+  }
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return ATTN_E_LAUNCH;
+  return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, D, scale, in_dtype, flags, nsplit,
+                     ws, cap, stream);
 }
 
 }  // extern "C"

@@ -272,6 +272,28 @@ int attn_split_range(int64_t Lk, int64_t nsplit, int64_t s, int64_t* begin, int6
  * 256-byte boundary: the per-split state of split-K (SyclKittens summary, section E.2). */
 int64_t attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Lq, int64_t D, int64_t nsplit);
 
+/*
+ * attn_fwd_ex_noalloc -- attn_fwd_ex without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The partial results of a split launch go to a fixed array of
+ * ATTN_NOALLOC_WORKSPACE_BYTES owned by the library: one per GPU, created when the library
+ * is loaded and held until the process ends.  No call allocates or frees anything.
+ *   nsplit  as attn_fwd_ex; an explicit count whose partials need more than
+ *           ATTN_NOALLOC_WORKSPACE_BYTES (attn_workspace_bytes) is refused with
+ *           ATTN_E_WORKSPACE; with 0 the planner's count is used when its partials fit,
+ *           otherwise the largest count that fits (1, a single pass, always does).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and must be ordered by the caller.  Nothing in
+ * the array needs to start at zero (each split launch writes every partial it merges).
+ * Other arguments, results and codes as attn_fwd_ex; ATTN_E_LAUNCH also when the HIP
+ * runtime cannot give the array's address on the current device.
+ */
+#define ATTN_NOALLOC_WORKSPACE_BYTES (64ll << 20)
+int attn_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t D,
+                        float scale, int in_dtype, uint32_t flags, int64_t nsplit,
+                        void* stream);
+
 /* Dense fp16/bf16 MFMA peak of the current HIP device: compute units x peak shader clock x
  * 4096 flop per clock per compute unit (the gfx950 rate of v_mfma_f32_32x32x16_{f16,bf16}).
  * Any pointer may be NULL.  Returns ATTN_OK, or ATTN_E_LAUNCH if the HIP runtime reports no
