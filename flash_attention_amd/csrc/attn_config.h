@@ -12,6 +12,13 @@
 
 namespace attn_cfg {
 
+#ifndef ATTN_SYNC_BACK_256
+#define ATTN_SYNC_BACK_256 4
+#endif
+#ifndef ATTN_SYNC_BACK_128
+#define ATTN_SYNC_BACK_128 4
+#endif
+
 template <int D, int V>
 struct Tile;
 
@@ -27,6 +34,7 @@ struct Tile<128, 0> {
   static constexpr int BN = 32;     // keys per LDS tile
   static constexpr int STAGES = 4;  // K/V tiles resident in LDS at once
   static constexpr int WG_PER_CU = 1;  // workgroups per compute unit (registers, LDS)
+  static constexpr int SYNC_BACK = ATTN_SYNC_BACK_128;  // P.V steps after the tile barrier
 };
 
 // HD=256: four wavefronts (one per SIMD) of two 32-row query blocks each, so that every K
@@ -39,6 +47,7 @@ struct Tile<256, 0> {
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
   static constexpr int WG_PER_CU = 1;
+  static constexpr int SYNC_BACK = ATTN_SYNC_BACK_256;
 };
 
 // Narrow HD=128: four wavefronts of one 32-row block; 64 KiB of LDS and half the register
@@ -51,6 +60,7 @@ struct Tile<128, 1> {
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
   static constexpr int WG_PER_CU = 2;
+  static constexpr int SYNC_BACK = 4;
 };
 
 // Narrow HD=256: four wavefronts of one 32-row block (128 accumulator registers); the
@@ -62,6 +72,7 @@ struct Tile<256, 1> {
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
   static constexpr int WG_PER_CU = 1;
+  static constexpr int SYNC_BACK = 8;
 };
 
 template <int D, int V>

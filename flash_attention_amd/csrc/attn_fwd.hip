@@ -35,8 +35,8 @@
 // staging) into rings of four stages.  Iteration t of the key loop reads K of tile t (S^T)
 // and V of tile t-1 (the P.V product of the previous tile, under which the softmax of tile
 // t runs, one slice after each MFMA); tile t+1 is landing, and tile t+2 is copied after
-// the one workgroup barrier of the iteration, the waves taking turns over the last four
-// steps.  At HD=256 each wavefront owns 64 query rows (two 32-row MFMA blocks), so every
+// the one workgroup barrier of the iteration, one copy per MFMA window and no branch
+// around any of them.  At HD=256 each wavefront owns 64 query rows (two 32-row MFMA blocks), so every
 // K and V fragment read from LDS feeds two MFMAs (in the wide shape); at HD=128 two
 // wavefronts of 32 rows share each SIMD, the one in its S^T phase at the higher issue
 // priority.  Q stays in registers and the output accumulator in pinned AGPRs for the whole
@@ -220,16 +220,6 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t
                : "memory");
 }
 
-// Same copy with a wave-uniform extra offset soffset (added to the address, not range
-// checked): used only where every byte read lies inside the buffer.
-__device__ __forceinline__ void lds_dma16_so(i32x4 rsrc, uint32_t voffset, uint32_t soffset,
-                                             uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_dst), "v"(voffset), "s"(rsrc), "s"(soffset)
-               : "memory");
-}
-
 // Growth threshold of the lazy rescale.  The exponentials use a per-row reference m: the
 // first key tile's maximum, raised only when a later tile outgrows it by this factor.  All
 // weights are non-negative, so a lane whose partial sum over a tile stays at or below the
@@ -327,7 +317,6 @@ void attn_fwd_kernel(Params p) {
   const int imax = __builtin_amdgcn_readfirstlane(max_pos(qtile * BM, qlast));
   const int kend = min(min(Lk, kbeg + p.split_len), imax + p.diag + 1);
   const int ntiles = kend > kbeg ? (kend - kbeg + BN - 1) / BN : 0;
-  const int nfull = (Lk - kbeg) / BN;  // tiles whose 32 rows all exist in K and V
 
   const uint16_t* qh = p.q + (size_t)bh * p.Lq * D;
   const uint16_t* kh = p.k + (((size_t)b * p.Hkv + hkv) * p.Lk + kbeg) * D;
@@ -356,7 +345,13 @@ void attn_fwd_kernel(Params p) {
       vk[par] = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_k(par * ROWS_PER_LOAD + r0)) * 16);
     vv = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
   }
-  const uint32_t kv_bytes = static_cast<uint32_t>(Lk - kbeg) * D * 2;
+  // Bytes of K (V) this workgroup may copy: its tiles, cut at the end of K (V).  Copies past
+  // them read zeros (the key loop issues the copies of tiles t+2 without checking t+2 <
+  // ntiles, which would cost a branch per copy).
+  // (64-bit: ntiles*TILE*2 reaches 2^32 at the longest key sequences; the K bytes stay
+  // below it)
+  const uint32_t kv_lim = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      min(static_cast<uint64_t>(Lk - kbeg) * D * 2, static_cast<uint64_t>(ntiles) * TILE * 2)));
   // K and V base addresses of this head as wave-uniform 64-bit values (scalar registers),
   // so that the per-tile descriptors are scalar arithmetic.
   auto uniform64 = [](const void* ptr) {
@@ -366,49 +361,37 @@ void attn_fwd_kernel(Params p) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
   };
   const uint64_t kb = uniform64(kh), vb = uniform64(vh);
-  // Descriptor of the buffer that starts skip bytes into K (V) and holds the rest of it,
-  // computed with scalar instructions (the compiler would otherwise use 64-bit vector adds
-  // and move the results back).
-  auto rsrc_at = [&](uint64_t base, uint32_t skip) {
-    uint32_t lo, hi, n;
-    asm("s_add_u32 %0, %3, %5\n\ts_addc_u32 %1, %4, 0\n\ts_sub_u32 %2, %6, %5"
-        : "=&s"(lo), "=&s"(hi), "=&s"(n)
-        : "s"(static_cast<uint32_t>(base)), "s"(static_cast<uint32_t>(base >> 32)),
-          "s"(__builtin_amdgcn_readfirstlane(skip)), "s"(kv_bytes)
-        : "scc");
-    return (i32x4){static_cast<int>(lo), static_cast<int>(hi), static_cast<int>(n), 0x00020000};
-  };
-  auto issue_tile = [&](int t, int st) {
+  // Copy j (0 <= j < 2*LOADS) of this thread's share of tile t, into stage st: K copy
+  // round j/2 for even j, V round j/2 for odd j.  Branch-free: the round's first byte,
+  // off = t*TILE*2 + row offset, moves the descriptor's base (scalar arithmetic), and its
+  // size is what is left of the workgroup's bytes past it, clamped at 0, so rows past them
+  // (past Lk in a partial last tile, or a tile t past the last one) read as zeros and touch
+  // no memory.
+  auto issue_copy = [&](int t, int st, int j) {
     // (laundered: the destinations are added here, not kept per stage in scalar registers)
     uint32_t ks = lds_base + static_cast<uint32_t>(st * 2 * TILE);
     asm volatile("" : "+s"(ks));
-    const uint32_t vs = ks + NSTAGE * 2 * TILE;
-    const uint32_t skip = static_cast<uint32_t>(t) * TILE * 2;  // t < ntiles: skip < kv_bytes
-    const i32x4 rk = rsrc_at(kb, skip);
-    const i32x4 rv = rsrc_at(vb, skip);
-    if (t < nfull) {
-      // All 32 rows exist: the per-round row offset goes into the scalar offset and every
-      // copy uses the lane's fixed offset (no vector arithmetic, no reuse of one register).
+    const bool isv = j & 1;
+    const int i = j >> 1;
+    const uint32_t dst = (isv ? ks + NSTAGE * 2 * TILE : ks) + (i * THREADS + wave * 64) * 16;
+    // (64-bit, clamped: the tiles past the last one may lie past 2^32 bytes)
+    const uint32_t off = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        min(static_cast<uint64_t>(t) * TILE * 2 + i * ROWS_PER_LOAD * D * 2,
+            static_cast<uint64_t>(kv_lim))));
+    const uint64_t base = isv ? vb : kb;
+    uint32_t lo, hi, n;
+    asm("s_add_u32 %0, %3, %5\n\ts_addc_u32 %1, %4, 0\n\ts_sub_u32 %2, %6, %5\n\t"
+        "s_cselect_b32 %2, 0, %2"
+        : "=&s"(lo), "=&s"(hi), "=&s"(n)
+        : "s"(static_cast<uint32_t>(base)), "s"(static_cast<uint32_t>(base >> 32)), "s"(off),
+          "s"(kv_lim)
+        : "scc");
+    const i32x4 r = {static_cast<int>(lo), static_cast<int>(hi), static_cast<int>(n), 0x00020000};
+    lds_dma16(r, isv ? vv : vk[i & 1], dst);
+  };
+  auto issue_tile = [&](int t, int st) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const uint32_t slot0 = (i * THREADS + wave * 64) * 16;  // wave-uniform
-        const uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
-        lds_dma16_so(rk, vk[i & 1], rows, ks + slot0);
-        lds_dma16_so(rv, vv, rows, vs + slot0);
-      }
-    } else {
-      // The partial last tile: rows past Lk must fall outside the buffer and read as zero,
-      // so the row offset goes into the range-checked per-lane offset.
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const uint32_t slot0 = (i * THREADS + wave * 64) * 16;
-        // (rows laundered: added here, not hoisted into loop-invariant registers)
-        uint32_t rows = static_cast<uint32_t>(i * ROWS_PER_LOAD * D * 2);
-        asm volatile("" : "+s"(rows));
-        lds_dma16(rk, vk[i & 1] + rows, ks + slot0);
-        lds_dma16(rv, vv + rows, vs + slot0);
-      }
-    }
+    for (int j = 0; j < 2 * LOADS; ++j) issue_copy(t, st, j);
   };
 
   // With two wavefronts per SIMD (HD=128) a wavefront has 256 registers, which the compiler
@@ -666,11 +649,13 @@ void attn_fwd_kernel(Params p) {
 
   // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
   // (PV) with the softmax of tile t in slices underneath.
-  // P.V step of the synchronisation point: four steps before the end, so that the copies
-  // issued after it have most of an iteration to land; the waves issue them in turn,
-  // WAVES/4 per step.
-  constexpr int SYNC_STEP = NSTEP - 4;
-  constexpr int COPY_WAVES = WAVES / 4;  // waves issuing copies per step
+  // P.V step of the synchronisation point: SYNC_BACK steps before the end.  The copies of
+  // tile t+2 are issued in the sub-steps from there on, one per MFMA window: copy j in
+  // sub-step QB*SYNC_STEP + j*SPACING, the same windows in every wave (no branch).
+  constexpr int SYNC_STEP = NSTEP - attn_cfg::Tile<D, V>::SYNC_BACK;
+  constexpr int NCOPY = 2 * LOADS;  // copies per thread and tile
+  constexpr int SPACING = QB * attn_cfg::Tile<D, V>::SYNC_BACK / NCOPY;
+  static_assert(SYNC_STEP >= 1 && SPACING >= 1, "a window after the sync point per copy");
   u32x4 kf[3];
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
   auto iteration = [&](auto pv_tag, auto st_tag, int t, u32x4 (&pprev)[QB][2],
@@ -690,10 +675,6 @@ void attn_fwd_kernel(Params p) {
     // after an MFMA overlaps it only until the next MFMA: one sub-step per MFMA gives
     // every MFMA its own window.  Exponentials (quarter-rate) are spread one or two per
     // window over all sub-steps after the first (tile 0: after its row maxima).
-    // (the wave index laundered per iteration: the compiler would otherwise keep one
-    // loop-invariant lane mask per copy step, and spill them)
-    int wv = wave;
-    asm volatile("" : "+s"(wv));
     constexpr int H = QB * NSTEP;                 // sub-steps
     constexpr int EXP0 = PV ? 1 : QB + 1;         // first sub-step with exponentials
 #pragma unroll
@@ -720,11 +701,10 @@ void attn_fwd_kernel(Params p) {
           exp_slice(sacc, pcur, NELEM * (h - EXP0) / (H - EXP0),
                     NELEM * (h - EXP0 + 1) / (H - EXP0));
         if (h == QB * SYNC_STEP) sync_point(t);
-        // copies of tile t+2 in the steps from the synchronisation point on, a few waves
-        // per step, so that the waves' copies do not queue up behind each other
-        static_assert(WAVES % 4 == 0, "waves share the four copy steps evenly");
-        if (hb == QB - 1 && s >= SYNC_STEP && t + 2 < ntiles && wv / COPY_WAVES == s - SYNC_STEP)
-          issue_tile(t + 2, (ST + 2) % NSTAGE);
+        // copies of tile t+2, one per window from the synchronisation point on
+        if (h >= QB * SYNC_STEP && (h - QB * SYNC_STEP) % SPACING == 0 &&
+            (h - QB * SYNC_STEP) / SPACING < NCOPY)
+          issue_copy(t + 2, (ST + 2) % NSTAGE, (h - QB * SYNC_STEP) / SPACING);
         if (h == H - 1) {
           if constexpr (PV) rescale_if_grown(kstage(ST), t, pcur);
 #pragma unroll
@@ -788,6 +768,9 @@ void attn_fwd_kernel(Params p) {
     }
     if (ntiles & 1) drain(ntiles - 1, pa);  // P(t) lives in pa for even t
     else drain(ntiles - 1, pb2);
+    // the last iterations copied (zeros) for tiles past the end: let them land before the
+    // workgroup's LDS is released
+    WAIT_VMCNT(0);
   }
 
   // Epilogue: O = O^T / l (one reciprocal per row), LSE = ln2 * (m + log2 l).  An empty
