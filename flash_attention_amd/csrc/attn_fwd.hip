@@ -132,11 +132,11 @@ struct Elt<_Float16> {
     f16x2 r = __builtin_convertvector((f32x2){x, y}, f16x2);
     return __builtin_bit_cast(uint32_t, r);
   }
-  // Row-sum update by a pair of weights x, y whose rounded values are packed in w: fp16
-  // rounding (relative 2^-11) keeps the log-sum-exp well inside its tolerance, so the sum
-  // takes the packed values in one v_dot2 with (1, 1), accumulating in fp32.
-  static __device__ __forceinline__ float sum2(uint32_t w, float, float, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), (f16x2){1, 1}, acc, false);
+  // Row-sum update by a pair of weights x, y: their fp32 values (a v_dot2 of the packed
+  // 16-bit values would be one instruction instead of two, but on gfx950 each dot
+  // instruction placed between MFMAs holds the matrix pipe for ~20 cycles).
+  static __device__ __forceinline__ float sum2(uint32_t, float x, float y, float acc) {
+    return acc + (x + y);
   }
 };
 
@@ -150,7 +150,7 @@ struct Elt<__bf16> {
     bf16x2 r = __builtin_convertvector((f32x2){x, y}, bf16x2);
     return __builtin_bit_cast(uint32_t, r);
   }
-  // bf16 rounding (2^-8) would move the log-sum-exp by up to ~4e-3: sum the fp32 values.
+  // The fp32 values (bf16 rounding, 2^-8, would move the log-sum-exp by up to ~4e-3).
   static __device__ __forceinline__ float sum2(uint32_t, float x, float y, float acc) {
     return acc + (x + y);
   }
@@ -463,7 +463,9 @@ void attn_fwd_kernel(Params p) {
   // VALU work fills the gaps (measured: +1.6 % at 8K x 8K, +3.7 % of the cycles with the
   // clock unconstrained; the level does not matter).
   constexpr bool kShareSimd = attn_cfg::waves_per_simd<D, V>() > 1;
-  auto qk = [&](const char* ks, f32x16 (&sacc)[QB], u32x4 (&kf)[3], auto&& tail_loads) {
+  // window(w) places VALU work after MFMA w (w = kk*QB + qb) of the phase, to run under it.
+  auto qk = [&](const char* ks, f32x16 (&sacc)[QB], u32x4 (&kf)[3], auto&& tail_loads,
+                auto&& window) {
     if constexpr (kShareSimd) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -478,11 +480,14 @@ void attn_fwd_kernel(Params p) {
           if (kk == 0) Elt<T>::mfma_v0(kf[kk % 3], qf[qb][kk], sacc[qb]);
           else Elt<T>::mfma_v(kf[kk % 3], qf[qb][kk], sacc[qb]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        window(kk * QB + qb);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kShareSimd) __builtin_amdgcn_s_setprio(0);
   };
+  auto no_window = [](int) {};
   // One P.V step s of a tile: V^T fragment (32 dims x 16 keys) for MFMA step s, times both
   // P^T blocks.  MFMA step ks covers keys 16ks..16ks+15; its P^T operand is accumulator
   // registers 8ks..8ks+7, whose keys for lane half h are 16ks + {4h..4h+3, 8+4h..8+4h+3}:
@@ -573,34 +578,46 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m[qb] = m[qb] == -__builtin_inff() ? 0.f : m[qb];
   };
-  float ev[QB][16], lt[QB];
-  auto exp_slice = [&](f32x16 (&sacc)[QB], u32x4 (&pcur)[QB][2], int e0, int e1) {
+  // Weights of a tile in two halves.  Under the P.V MFMAs of iteration t: the exponentials
+  // of tile t, ew = exp2(c*s - m), kept in fp32 (element e: register e%16 of query block
+  // e/16).  Under the S^T MFMAs of iteration t+1, whose windows have no other VALU work:
+  // ew rounded to 16 bits in the register layout of the P^T operand (pw), the partial row
+  // sums lt, and the growth check, just before the P.V MFMAs of iteration t+1 read pw.
+  float ew[QB][16], lt[QB];
+  u32x4 pw[QB][2];
+  auto exp_slice = [&](f32x16 (&sacc)[QB], int e0, int e1) {
 #pragma unroll
-    for (int e = e0; e < e1; ++e) {  // element e: register e%16 of query block e/16
+    for (int e = e0; e < e1; ++e) {
       const int qb = e >> 4, r = e & 15;
-      ev[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -m[qb]));
-      if (r & 1) {
-        uint32_t w = Elt<T>::pack2(ev[qb][r - 1], ev[qb][r]);
-        pin(w);
-        // this tile's part of the row sum (lane-local 16 keys)
-        lt[qb] = Elt<T>::sum2(w, ev[qb][r - 1], ev[qb][r], r == 1 ? 0.f : lt[qb]);
-        pcur[qb][r >> 3][(r & 7) >> 1] = w;
-      }
+      ew[qb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c, -m[qb]));
+      pin(ew[qb][r]);
     }
   };
-  // Lazy rescale after the exponentials of a tile t >= 1: the deferred compensation of the
-  // online softmax ("Key Optimization Insights / What Worked" of the HD=256 page), done
-  // only where a tile's scores outgrow the reference.  A lane whose partial sum of the
-  // tile's weights exceeds kGrowth holds a weight above it (weights are non-negative).  If
-  // any lane of the wave does, the wave raises each row's reference to the tile's maximum
-  // where that is larger, m' = max(m, mt), multiplies the row's output accumulator and
-  // sum by exp2(m - m') <= 1, and recomputes the tile's weights against m' (now at most
-  // 1).  The accumulator then holds tiles 0..t-1 against m', as the P.V product of tile t
-  // expects.  The scores themselves are not kept for this rare case (32 registers the wide
-  // HD=256 shape does not have): they are computed again from K(t), which stays in its LDS
-  // stage until tile t+4 is copied.  Each wave decides for its own rows; no other wave
-  // waits beyond the next barrier.
-  auto rescale_if_grown = [&](const char* ks, int t, u32x4 (&pcur)[QB][2]) {
+  // pairs p0..p1-1 of ew (pair p: elements 2p, 2p+1) into pw, with their partial row sums
+  auto pack_slice = [&](int p0, int p1) {
+#pragma unroll
+    for (int p = p0; p < p1; ++p) {
+      const int qb = (2 * p) >> 4, r = (2 * p) & 15;
+      uint32_t w = Elt<T>::pack2(ew[qb][r], ew[qb][r + 1]);
+      pin(w);
+      // this tile's part of the row sum (lane-local 16 keys)
+      lt[qb] = Elt<T>::sum2(w, ew[qb][r], ew[qb][r + 1], r == 0 ? 0.f : lt[qb]);
+      pw[qb][r >> 3][(r & 7) >> 1] = w;
+    }
+  };
+  // Lazy rescale of tile tp, after its weights are packed (the deferred compensation of the
+  // online softmax, "Key Optimization Insights / What Worked" of the HD=256 page, done only
+  // where a tile's scores outgrow the reference).  A lane whose partial sum of the tile's
+  // weights exceeds kGrowth holds a weight above it (weights are non-negative).  For each
+  // query block where any lane does, the wave raises each row's reference to the tile's
+  // maximum where that is larger, m' = max(m, mt), multiplies the row's output accumulator
+  // and sum by exp2(m - m') <= 1, and recomputes the tile's weights against m' (now at most
+  // 1).  The accumulator then holds tiles 0..tp-1 against m', as the P.V product of tile tp
+  // expects.  The scores of tile tp are computed again from K(tp), still in its LDS stage
+  // (until tile tp+4 is copied), into sacc; sacc held the scores of tile tp+1, which are
+  // then computed once more from K(tp+1) (ksr; nullptr: nothing to restore).  Each wave
+  // decides for its own rows; no other wave waits beyond the next barrier.
+  auto rescale_if_grown = [&](int tp, const char* ksp, const char* ksr, f32x16 (&sacc)[QB]) {
     bool grown[QB], any = false;  // per query block, wave-uniform
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -608,33 +625,38 @@ void attn_fwd_kernel(Params p) {
       any |= grown[qb];
     }
     if (!any) return;
-    f32x16 s2[QB];
     u32x4 kf2[3];
-    kf2[0] = kfrag(ks, 0);
-    kf2[1] = kfrag(ks, 1);
-    qk(ks, s2, kf2, [] {});
-    mfma_fence_v(s2);
-    mask_keys(s2, t);
+    kf2[0] = kfrag(ksp, 0);
+    kf2[1] = kfrag(ksp, 1);
+    qk(ksp, sacc, kf2, [] {}, no_window);
+    mfma_fence_v(sacc);
+    mask_keys(sacc, tp);
     attn_agpr::fence();  // the last P.V MFMA's results have landed
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (!grown[qb]) continue;  // that block's rows keep their reference
-      row_max(s2, qb);
+      row_max(sacc, qb);
       const float mn = fmaxf(m[qb], mt[qb]);
       const float delta = __builtin_amdgcn_exp2f(m[qb] - mn);
       m[qb] = mn;
       l[qb] *= delta;
-      // this block's weights and partial sums against m', a pair at a time (the scheduling
-      // barriers keep the compiler from computing all of them before packing any)
+      // this block's weights against m', a pair at a time (the scheduling barriers keep the
+      // compiler from computing all of them before packing any)
 #pragma unroll
       for (int e = 16 * qb; e < 16 * qb + 16; e += 2) {
-        exp_slice(s2, pcur, e, e + 2);
+        exp_slice(sacc, e, e + 2);
+        pack_slice(e / 2, e / 2 + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) attn_agpr::scale(qb * DB + db, delta);
     }
     attn_agpr::fence_write();
+    if (ksr != nullptr) {
+      kf2[0] = kfrag(ksr, 0);
+      kf2[1] = kfrag(ksr, 1);
+      qk(ksr, sacc, kf2, [] {}, no_window);
+    }
   };
 
   // Synchronisation point of iteration t (near the end of its P.V steps): tile t+1 has
@@ -657,26 +679,37 @@ void attn_fwd_kernel(Params p) {
   constexpr int SPACING = QB * attn_cfg::Tile<D, V>::SYNC_BACK / NCOPY;
   static_assert(SYNC_STEP >= 1 && SPACING >= 1, "a window after the sync point per copy");
   u32x4 kf[3];
+  constexpr int NPAIR = NELEM / 2;  // packed weight pairs per lane and tile
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
-  auto iteration = [&](auto pv_tag, auto st_tag, int t, u32x4 (&pprev)[QB][2],
-                       u32x4 (&pcur)[QB][2], f32x16 (&sacc)[QB]) {
+  auto iteration = [&](auto pv_tag, auto st_tag, int t, f32x16 (&sacc)[QB]) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
     constexpr int VST = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
     u32x4 vf[3];
-    qk(kstage(ST), sacc, kf, [&]() {
-      if constexpr (PV) {
-        vf[0] = vfrag_load(VST, 0);
-        vf[1] = vfrag_load(VST, 1);
-      }
-    });
+    // S^T(t), the weights of tile t-1 packed under its MFMAs
+    constexpr int W = QB * KS;  // S^T windows
+    qk(kstage(ST), sacc, kf,
+       [&]() {
+         if constexpr (PV) {
+           vf[0] = vfrag_load(VST, 0);
+           vf[1] = vfrag_load(VST, 1);
+         }
+       },
+       [&](int w) {
+         if constexpr (PV) pack_slice(NPAIR * w / W, NPAIR * (w + 1) / W);
+       });
+    if constexpr (PV) {
+      rescale_if_grown(t - 1, kstage(VST), kstage(ST), sacc);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
+    }
     // Each P.V step is QB sub-steps: one MFMA (query block qb), then a slice of VALU or
     // copy work that issues while that MFMA runs.  A wave issues in order, so work placed
     // after an MFMA overlaps it only until the next MFMA: one sub-step per MFMA gives
-    // every MFMA its own window.  Exponentials (quarter-rate) are spread one or two per
-    // window over all sub-steps after the first (tile 0: after its row maxima).
-    constexpr int H = QB * NSTEP;                 // sub-steps
-    constexpr int EXP0 = PV ? 1 : QB + 1;         // first sub-step with exponentials
+    // every MFMA its own window.  Exponentials are spread about one per window over all
+    // sub-steps after the first (tile 0: after its row maxima).
+    constexpr int H = QB * NSTEP;          // sub-steps
+    constexpr int EXP0 = PV ? 1 : QB + 1;  // first sub-step with exponentials
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       if constexpr (PV) {
@@ -685,7 +718,7 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
       for (int hb = 0; hb < QB; ++hb) {
         const int h = QB * s + hb;
-        if constexpr (PV) Elt<T>::acc_mfma(hb * DB + (s >> 1), vf[s % 3], pprev[hb][s & 1]);
+        if constexpr (PV) Elt<T>::acc_mfma(hb * DB + (s >> 1), vf[s % 3], pw[hb][s & 1]);
         __builtin_amdgcn_sched_barrier(0);
         if (h == 0) {
           mfma_fence_v(sacc);
@@ -698,30 +731,28 @@ void attn_fwd_kernel(Params p) {
           finite_reference();
         }
         if (h >= EXP0)
-          exp_slice(sacc, pcur, NELEM * (h - EXP0) / (H - EXP0),
-                    NELEM * (h - EXP0 + 1) / (H - EXP0));
+          exp_slice(sacc, NELEM * (h - EXP0) / (H - EXP0), NELEM * (h - EXP0 + 1) / (H - EXP0));
         if (h == QB * SYNC_STEP) sync_point(t);
         // copies of tile t+2, one per window from the synchronisation point on
         if (h >= QB * SYNC_STEP && (h - QB * SYNC_STEP) % SPACING == 0 &&
             (h - QB * SYNC_STEP) / SPACING < NCOPY)
           issue_copy(t + 2, (ST + 2) % NSTAGE, (h - QB * SYNC_STEP) / SPACING);
-        if (h == H - 1) {
-          if constexpr (PV) rescale_if_grown(kstage(ST), t, pcur);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
-          if (t + 1 < ntiles) {
-            // first two K fragments of tile t+1 (landed at the sync point)
-            kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
-            kf[1] = kfrag(kstage((ST + 1) % NSTAGE), 1);
-          }
+        if (h == H - 1 && t + 1 < ntiles) {
+          // first two K fragments of tile t+1 (landed at the sync point)
+          kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
+          kf[1] = kfrag(kstage((ST + 1) % NSTAGE), 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  // P.V of the last tile (no softmax, no synchronisation).
-  auto drain = [&](int t, u32x4 (&pprev)[QB][2]) {
+  // The last tile: its weights packed (with the growth check), then its P.V product.
+  auto drain = [&](int t, f32x16 (&sacc)[QB]) {
     const int st = t % NSTAGE;
+    pack_slice(0, NPAIR);
+    rescale_if_grown(t, kstage(st), nullptr, sacc);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
     u32x4 vf[3];
     vf[0] = vfrag_load(st, 0);
     vf[1] = vfrag_load(st, 1);
@@ -730,7 +761,7 @@ void attn_fwd_kernel(Params p) {
       if (s + 2 < NSTEP) vf[(s + 2) % 3] = vfrag_load(st, s + 2);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pprev[qb][s & 1]);
+        Elt<T>::acc_mfma(qb * DB + (s >> 1), vf[s % 3], pw[qb][s & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -738,9 +769,7 @@ void attn_fwd_kernel(Params p) {
   // The weights use a per-row reference m set by the first key tile instead of a maximum
   // kept up to date at every tile, so the output accumulator is rescaled only in the rare
   // tile whose scores outgrow m by more than a factor kGrowth (rescale_if_grown).  The loop
-  // is unrolled by four: the stage of each iteration is a compile-time constant and the two
-  // P buffers swap roles without copies.
-  u32x4 pa[QB][2], pb2[QB][2];
+  // is unrolled by four: the stage of each iteration is a compile-time constant.
   f32x16 sacc[QB];  // scores of the current tile
   // (a workgroup with no key to look at, under the causal mask or past the last split,
   // skips the loop: its rows are empty)
@@ -754,20 +783,19 @@ void attn_fwd_kernel(Params p) {
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
-    iteration(std::false_type{}, S0{}, 0, pb2, pa, sacc);
+    iteration(std::false_type{}, S0{}, 0, sacc);
     int t = 1;
-    while (t < ntiles) {  // P(t-1) in pa for odd t, in pb2 for even t
-      iteration(std::true_type{}, S1{}, t, pa, pb2, sacc);
+    while (t < ntiles) {
+      iteration(std::true_type{}, S1{}, t, sacc);
       if (++t >= ntiles) break;
-      iteration(std::true_type{}, S2{}, t, pb2, pa, sacc);
+      iteration(std::true_type{}, S2{}, t, sacc);
       if (++t >= ntiles) break;
-      iteration(std::true_type{}, S3{}, t, pa, pb2, sacc);
+      iteration(std::true_type{}, S3{}, t, sacc);
       if (++t >= ntiles) break;
-      iteration(std::true_type{}, S0{}, t, pb2, pa, sacc);
+      iteration(std::true_type{}, S0{}, t, sacc);
       ++t;
     }
-    if (ntiles & 1) drain(ntiles - 1, pa);  // P(t) lives in pa for even t
-    else drain(ntiles - 1, pb2);
+    drain(ntiles - 1, sacc);
     // the last iterations copied (zeros) for tiles past the end: let them land before the
     // workgroup's LDS is released
     WAIT_VMCNT(0);
