@@ -12,13 +12,6 @@
 
 namespace attn_cfg {
 
-#ifndef ATTN_SYNC_BACK_256
-#define ATTN_SYNC_BACK_256 4
-#endif
-#ifndef ATTN_SYNC_BACK_128
-#define ATTN_SYNC_BACK_128 4
-#endif
-
 template <int D, int V>
 struct Tile;
 
@@ -34,7 +27,6 @@ struct Tile<128, 0> {
   static constexpr int BN = 32;     // keys per LDS tile
   static constexpr int STAGES = 4;  // K/V tiles resident in LDS at once
   static constexpr int WG_PER_CU = 1;  // workgroups per compute unit (registers, LDS)
-  static constexpr int SYNC_BACK = ATTN_SYNC_BACK_128;  // P.V steps after the tile barrier
 };
 
 // HD=256: four wavefronts (one per SIMD) of two 32-row query blocks each, so that every K
@@ -47,7 +39,6 @@ struct Tile<256, 0> {
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
   static constexpr int WG_PER_CU = 1;
-  static constexpr int SYNC_BACK = ATTN_SYNC_BACK_256;
 };
 
 // Narrow HD=128: four wavefronts of one 32-row block; 64 KiB of LDS and half the register
@@ -60,7 +51,6 @@ struct Tile<128, 1> {
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
   static constexpr int WG_PER_CU = 2;
-  static constexpr int SYNC_BACK = 4;
 };
 
 // Narrow HD=256: four wavefronts of one 32-row block (128 accumulator registers); the
@@ -72,7 +62,6 @@ struct Tile<256, 1> {
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
   static constexpr int WG_PER_CU = 1;
-  static constexpr int SYNC_BACK = 8;
 };
 
 template <int D, int V>

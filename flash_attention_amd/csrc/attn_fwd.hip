@@ -33,10 +33,10 @@
 //
 // Pipeline.  K and V tiles of 32 keys are copied straight from HBM into LDS (no register
 // staging) into rings of four stages.  Iteration t of the key loop reads K of tile t (S^T)
-// and V of tile t-1 (the P.V product of the previous tile, under which the softmax of tile
-// t runs, one slice after each MFMA); tile t+1 is landing, and tile t+2 is copied after
-// the one workgroup barrier of the iteration, one copy per MFMA window and no branch
-// around any of them.  At HD=256 each wavefront owns 64 query rows (two 32-row MFMA blocks), so every
+// and V of tile t-1 (the P.V product of the previous tile).  Under the S^T MFMAs run the
+// copies of tile t+1 (one per few MFMA windows, no branch around any) and the rounding and
+// row sums of tile t-1's weights; under the P.V MFMAs, the exponentials of tile t.  The one
+// workgroup barrier of the iteration, at its end, makes tile t+1 visible to every wave.  At HD=256 each wavefront owns 64 query rows (two 32-row MFMA blocks), so every
 // K and V fragment read from LDS feeds two MFMAs (in the wide shape); at HD=128 two
 // wavefronts of 32 rows share each SIMD, the one in its S^T phase at the higher issue
 // priority.  Q stays in registers and the output accumulator in pinned AGPRs for the whole
@@ -242,7 +242,7 @@ void attn_fwd_kernel(Params p) {
                 "one 32-key block per tile");
   constexpr int THREADS = attn_cfg::threads<D, V>();
   constexpr int WAVES = attn_cfg::Tile<D, V>::WAVES;
-  static_assert(NSTAGE == 4, "tiles t-1 (V), t (K), t+1, t+2 (in flight) resident");
+  static_assert(NSTAGE == 4, "tiles t-1 (V), t (K), t+1 (landing) resident; a fourth stage keeps the unrolled loop's stage offsets static");
   constexpr int KS = D / 16;    // contraction steps of S^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -346,7 +346,7 @@ void attn_fwd_kernel(Params p) {
     vv = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
   }
   // Bytes of K (V) this workgroup may copy: its tiles, cut at the end of K (V).  Copies past
-  // them read zeros (the key loop issues the copies of tiles t+2 without checking t+2 <
+  // them read zeros (the key loop issues the copies of tile t+1 without checking t+1 <
   // ntiles, which would cost a branch per copy).
   // (64-bit: ntiles*TILE*2 reaches 2^32 at the longest key sequences; the K bytes stay
   // below it)
@@ -411,7 +411,6 @@ void attn_fwd_kernel(Params p) {
   }
 
   if (ntiles > 0) issue_tile(0, 0);
-  if (ntiles > 1) issue_tile(1, 1);
 
   // ---- per-lane LDS byte offsets of the fragment reads (stage base added later) ----
   // K (A operand of S^T): row l%32, chunk 2kk+hi at slot (2kk+hi) ^ sw, sw = swz_k(l%32);
@@ -659,25 +658,20 @@ void attn_fwd_kernel(Params p) {
     }
   };
 
-  // Synchronisation point of iteration t (near the end of its P.V steps): tile t+1 has
-  // landed everywhere and every wave is past iteration t-1, so the stage of tile t-2 can take
-  // tile t+2, copied in the steps after this point.
+  // Synchronisation point at the end of iteration t: tile t+1 (copied under this
+  // iteration's S^T MFMAs) has landed everywhere, and every wave is done with the V of tile
+  // t-1, so the next iteration may read tile t+1 and copy tile t+2 into the stage of tile
+  // t-2.
   auto sync_point = [&](int t) {
     if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of tile t+1
-    // A bare s_barrier: the LDS reads still in flight here (V fragments of tile t-1) touch
-    // no stage that is about to be overwritten, so they need not complete first.
+    // A bare s_barrier: every LDS read of this iteration has been waited for by the MFMA
+    // that consumed it.
     __builtin_amdgcn_s_barrier();
   };
 
   // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
   // (PV) with the softmax of tile t in slices underneath.
-  // P.V step of the synchronisation point: SYNC_BACK steps before the end.  The copies of
-  // tile t+2 are issued in the sub-steps from there on, one per MFMA window: copy j in
-  // sub-step QB*SYNC_STEP + j*SPACING, the same windows in every wave (no branch).
-  constexpr int SYNC_STEP = NSTEP - attn_cfg::Tile<D, V>::SYNC_BACK;
   constexpr int NCOPY = 2 * LOADS;  // copies per thread and tile
-  constexpr int SPACING = QB * attn_cfg::Tile<D, V>::SYNC_BACK / NCOPY;
-  static_assert(SYNC_STEP >= 1 && SPACING >= 1, "a window after the sync point per copy");
   u32x4 kf[3];
   constexpr int NPAIR = NELEM / 2;  // packed weight pairs per lane and tile
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
@@ -686,8 +680,11 @@ void attn_fwd_kernel(Params p) {
     constexpr int ST = decltype(st_tag)::value;
     constexpr int VST = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
     u32x4 vf[3];
-    // S^T(t), the weights of tile t-1 packed under its MFMAs
+    // S^T(t); under its MFMAs the weights of tile t-1 are packed, and the copies of tile
+    // t+1 issued into the stage of tile t-3 (free: every wave is past iteration t-1's
+    // barrier), copy j after MFMA j*W/NCOPY
     constexpr int W = QB * KS;  // S^T windows
+    static_assert(W % NCOPY == 0, "whole S^T windows per copy");
     qk(kstage(ST), sacc, kf,
        [&]() {
          if constexpr (PV) {
@@ -697,6 +694,7 @@ void attn_fwd_kernel(Params p) {
        },
        [&](int w) {
          if constexpr (PV) pack_slice(NPAIR * w / W, NPAIR * (w + 1) / W);
+         if (w % (W / NCOPY) == 0) issue_copy(t + 1, (ST + 1) % NSTAGE, w / (W / NCOPY));
        });
     if constexpr (PV) {
       rescale_if_grown(t - 1, kstage(VST), kstage(ST), sacc);
@@ -732,11 +730,7 @@ void attn_fwd_kernel(Params p) {
         }
         if (h >= EXP0)
           exp_slice(sacc, NELEM * (h - EXP0) / (H - EXP0), NELEM * (h - EXP0 + 1) / (H - EXP0));
-        if (h == QB * SYNC_STEP) sync_point(t);
-        // copies of tile t+2, one per window from the synchronisation point on
-        if (h >= QB * SYNC_STEP && (h - QB * SYNC_STEP) % SPACING == 0 &&
-            (h - QB * SYNC_STEP) / SPACING < NCOPY)
-          issue_copy(t + 2, (ST + 2) % NSTAGE, (h - QB * SYNC_STEP) / SPACING);
+        if (h == H - 1) sync_point(t);
         if (h == H - 1 && t + 1 < ntiles) {
           // first two K fragments of tile t+1 (landed at the sync point)
           kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
@@ -774,8 +768,7 @@ void attn_fwd_kernel(Params p) {
   // (a workgroup with no key to look at, under the causal mask or past the last split,
   // skips the loop: its rows are empty)
   if (ntiles > 0) {
-    if (ntiles > 1) WAIT_VMCNT(2 * LOADS);  // tile 0 landed (tile 1 may be in flight)
-    else WAIT_VMCNT(0);
+    WAIT_VMCNT(0);  // tile 0 landed
     __syncthreads();
     kf[0] = kfrag(kstage(0), 0);
     kf[1] = kfrag(kstage(0), 1);
@@ -796,7 +789,7 @@ void attn_fwd_kernel(Params p) {
       ++t;
     }
     drain(ntiles - 1, sacc);
-    // the last iterations copied (zeros) for tiles past the end: let them land before the
+    // the last iteration copied (zeros) for a tile past the end: let it land before the
     // workgroup's LDS is released
     WAIT_VMCNT(0);
   }
