@@ -119,6 +119,8 @@ def compare_rows(o_gpu, lse_gpu, rows, o_ref, lse_ref):
 # end of input) ends it; the median MHz of the samples (or "null") comes back on stdout.
 _SCLK_POLLER = r"""
 import json, shutil, subprocess, sys, threading
+sys.path.insert(0, sys.argv[1])
+from bench import sclk_from_csv
 exe = shutil.which("rocm-smi")
 if sys.stdin.readline().strip() != "start" or exe is None:
     print("null", flush=True)
@@ -132,17 +134,25 @@ while not stop.is_set():
                            timeout=20)
     except (OSError, subprocess.SubprocessError):
         break
-    lines = [x for x in r.stdout.splitlines() if "," in x]
-    if len(lines) >= 2:
-        head = lines[0].split(",")
-        if "sclk clock speed:" in head:
-            cell = lines[1].split(",")[head.index("sclk clock speed:")]
-            digits = "".join(ch for ch in cell if ch.isdigit())
-            if digits:
-                samples.append(int(digits))
+    mhz = sclk_from_csv(r.stdout)
+    if mhz:
+        samples.append(mhz)
     stop.wait(0.2)
 print(json.dumps(sorted(samples)[len(samples) // 2] if samples else None), flush=True)
 """
+
+
+def sclk_from_csv(text):
+    """Shader clock (MHz) of the first GPU from `rocm-smi --showclocks --csv`, or None."""
+    lines = [x for x in text.splitlines() if "," in x]
+    if len(lines) < 2:
+        return None
+    head = lines[0].split(",")
+    if "sclk clock speed:" not in head:
+        return None
+    cell = lines[1].split(",")[head.index("sclk clock speed:")]
+    digits = "".join(ch for ch in cell if ch.isdigit())
+    return int(digits) if digits else None
 
 
 def start_sclk_poller():
@@ -152,8 +162,8 @@ def start_sclk_poller():
     if "rocprof" in os.environ.get("LD_PRELOAD", ""):
         return None
     try:
-        return subprocess.Popen([sys.executable, "-c", _SCLK_POLLER], stdin=subprocess.PIPE,
-                                stdout=subprocess.PIPE, text=True)
+        return subprocess.Popen([sys.executable, "-c", _SCLK_POLLER, ROOT],
+                                stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True)
     except OSError:
         return None
 
@@ -261,6 +271,7 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    epoch0 = time.time()
     wall0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
@@ -268,6 +279,9 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    # (wall-clock bounds of the timed region, for a clock sampler outside this process)
+    print("[bench] timed region epoch %.3f %.3f" % (epoch0, epoch0 + wall), file=sys.stderr,
+          flush=True)
     ms_per_step = wall * 1e3 / args.steps
     kern_avg = e0.elapsed_time(e1) / args.steps
     flops = flops_workload(w)

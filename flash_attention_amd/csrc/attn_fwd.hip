@@ -399,18 +399,53 @@ void attn_fwd_kernel(Params p) {
   // only by the S^T MFMAs, then live in AGPRs next to the output accumulator.
   constexpr bool Q_AGPR = attn_cfg::waves_per_simd<D, V>() > 1;
   // Q^T operand fragments, register resident for the whole key loop: lane l holds query
-  // row l%32 of block qb, dims 16*kk + 8*(l/32) .. +7.  Rows past Lq re-read row Lq-1
-  // (never stored).
+  // row l%32 of block qb, dims 16*kk + 8*(l/32) .. +7.  Q is staged once in LDS: direct
+  // copies of 1 KiB of contiguous bytes each (loaded straight into this layout, every
+  // instruction would touch 32 rows), then one 16-byte LDS read per fragment.  A 32-row
+  // query block is as large as a K tile, so block b of the workgroup takes one stage slot,
+  // slot s at byte s*TILE*2 (the K stages 0-3, then the V stages 0-3).  The narrow shape's
+  // four blocks avoid the slots of tile 0 (K and V of stage 0), whose copies run beside
+  // Q's; the wide shape's eight fill the LDS, and tile 0 is copied once they are read.
+  // Within a slot, chunk c of row r sits at position c ^ (r % CPR): the 32 rows of one
+  // fragment read spread over distinct banks.  Rows past Lq re-read row Lq-1 (never
+  // stored).
+  constexpr int NQB = BM / 32;                           // query blocks per workgroup
+  constexpr bool Q_FILLS_LDS = NQB > 2 * NSTAGE - 2;     // tile 0 waits for Q
+  constexpr int QCOPY_PER_BLOCK = TILE * 2 / 1024;       // 1 KiB copies per block
+  constexpr int QCOPIES = NQB * QCOPY_PER_BLOCK / WAVES;  // per wave
+  static_assert(NQB <= 2 * NSTAGE && QCOPIES * WAVES == NQB * QCOPY_PER_BLOCK,
+                "Q fits the stage slots, in whole copies per wave");
+  auto qslot = [](int b) { return Q_FILLS_LDS ? b : b + 1 + (b >= NSTAGE - 1); };
+  {
+    const i32x4 qrsrc = make_rsrc(qh, static_cast<uint32_t>(p.Lq) * D * 2);
+    if (!Q_FILLS_LDS && ntiles > 0) issue_tile(0, 0);
+#pragma unroll
+    for (int j = 0; j < QCOPIES; ++j) {
+      const int n = wave + WAVES * j;
+      const int b = n / QCOPY_PER_BLOCK, i = n % QCOPY_PER_BLOCK;
+      const int pos = i * 1024 + 16 * lane;  // byte of the slot this lane fills
+      const int r = pos / (2 * D);
+      const int c = ((pos % (2 * D)) / 16) ^ (r % CPR);
+      const int row = min(qtile * BM + 32 * b + r, p.Lq - 1);
+      lds_dma16(qrsrc, static_cast<uint32_t>(row * D * 2 + 16 * c),
+                lds_base + static_cast<uint32_t>(qslot(b) * TILE * 2 + i * 1024));
+    }
+    WAIT_VMCNT(0);
+    __syncthreads();
+  }
   u32x4 qf[QB][KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int row = min(qrow0 + qb * 32 + l32, p.Lq - 1);
-    const u32x4* src = reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 8 * hi);
+    const char* qs = reinterpret_cast<const char*>(smem) + qslot(wave * QB + qb) * TILE * 2 +
+                     l32 * D * 2;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) qf[qb][kk] = src[2 * kk];
+    for (int kk = 0; kk < KS; ++kk)
+      qf[qb][kk] = *reinterpret_cast<const u32x4*>(qs + 16 * ((2 * kk + hi) ^ (l32 % CPR)));
   }
-
-  if (ntiles > 0) issue_tile(0, 0);
+  if constexpr (Q_FILLS_LDS) {
+    __syncthreads();  // every wave has its Q: the slots take tile 0
+    if (ntiles > 0) issue_tile(0, 0);
+  }
 
   // ---- per-lane LDS byte offsets of the fragment reads (stage base added later) ----
   // K (A operand of S^T): row l%32, chunk 2kk+hi at slot (2kk+hi) ^ sw, sw = swz_k(l%32);

@@ -1,12 +1,19 @@
-"""rocprofv3 harness for the attention kernel: MFMA utilisation, LDS bank conflicts, HBM
-traffic and bandwidth of one workload, from separate profiler runs of bench.py.
+"""rocprofv3 harness for the attention kernel: launch durations next to a bench line of the
+same run, MFMA utilisation, LDS bank conflicts and HBM traffic of one workload, from
+separate profiler runs of bench.py.
 
     python -m flash_attention_amd.rocprof_harness --workload gqa16k_d256 \
-        [--outdir rocprof_out] [--traffic-json traffic.json]
-    python -m flash_attention_amd.rocprof_harness --workload all --traffic-json traffic.json
+        [--outdir rocprof_out] [--traffic-json traffic.json] [--md summary.md]
+    python -m flash_attention_amd.rocprof_harness --workload all --traffic-json traffic.json \
+        [--md-dir profiles]
 
 Runs, each as its own child process (this process never touches the GPU):
-  1. rocprofv3 --kernel-trace --stats          -> launch durations of the kernel
+  1. rocprofv3 --kernel-trace --stats  -- bench.py (W warm-up + K timed launches)
+     -> every launch's duration and bench.py's own JSON line from the same process; the
+        average over the K timed launches (dispatch order: the first W launches of the
+        attention kernel are the warm-up) is set beside the bench line's event-timed mean.
+        Meanwhile this process samples the shader clock with rocm-smi; the median of the
+        samples inside the timed region (bench.py prints its wall-clock bounds) is recorded.
   2. rocprofv3 --pmc MfmaUtil LdsBankConflict  -> matrix-core busy %, LDS conflicts/access
   3. rocprofv3 --pmc FETCH_SIZE                -> KiB read from HBM per dispatch
   4. rocprofv3 --pmc WRITE_SIZE                -> KiB written to HBM per dispatch
@@ -15,22 +22,27 @@ of its known byte count to what the counter reads for it calibrates the counter,
 kernel's reading is scaled by that ratio.  Counter passes run under a hard kill timeout
 so that a refused counter request cannot leave a hung profiler behind.
 
-Prints a markdown summary and, with --traffic-json, records the calibrated bytes per
-launch under the workload's name together with the hash of the kernel sources, so that
-bench.py reports them only while the kernel is unchanged.
+Prints a markdown summary (also written to --md, or to <md-dir>/<kernel>__<workload>.md)
+and, with --traffic-json, records the calibrated bytes per launch under the workload's name
+together with the hash of the kernel sources, so that bench.py reports them only while the
+kernel is unchanged.
 """
 import argparse
 import csv
 import glob
 import json
 import os
+import shutil
 import statistics
 import subprocess
 import sys
+import threading
+import time
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 KERNEL_TAG = "attn_fwd_kernel"
+MERGE_TAG = "attn_merge_kernel"
 COPY_MIB = 1024
 
 
@@ -42,13 +54,18 @@ def _bench_cmd(workload, steps, warmup, calib):
     return cmd
 
 
-def _run(cmd, log, kill_after):
-    """Run one profiler pass from /tmp (TMPDIR=/tmp); return its exit status."""
+def _run(cmd, log, kill_after, out=None):
+    """Run one profiler pass from /tmp (TMPDIR=/tmp); return its exit status.  stdout goes
+    to `out` when given (bench.py's JSON line), else with stderr to `log`."""
     env = dict(os.environ, TMPDIR="/tmp")
     full = ["timeout", "-s", "KILL", str(kill_after)] + cmd
     print("[harness] " + " ".join(cmd), flush=True)
     with open(log, "w") as f:
-        r = subprocess.run(full, cwd="/tmp", env=env, stdout=f, stderr=subprocess.STDOUT)
+        if out is None:
+            r = subprocess.run(full, cwd="/tmp", env=env, stdout=f, stderr=subprocess.STDOUT)
+        else:
+            with open(out, "w") as g:
+                r = subprocess.run(full, cwd="/tmp", env=env, stdout=g, stderr=f)
     # rocprofv3 may end with SIGSEGV after the program finished and wrote its results
     print("[harness]   exit %d (log %s)" % (r.returncode, log), flush=True)
     return r.returncode
@@ -72,12 +89,19 @@ def counters(outdir, name):
     return res
 
 
-def kernel_durations(outdir):
-    ns = []
+def kernel_durations(outdir, tag=KERNEL_TAG):
+    """Durations (ns) of the launches whose name contains `tag`, in dispatch order."""
+    rows = [r for r in _rows(os.path.join(outdir, "trace", "**", "*kernel_trace.csv"))
+            if tag in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+
+
+def kernel_name(outdir, tag=KERNEL_TAG):
     for r in _rows(os.path.join(outdir, "trace", "**", "*kernel_trace.csv")):
-        if KERNEL_TAG in r["Kernel_Name"]:
-            ns.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    return ns
+        if tag in r["Kernel_Name"]:
+            return r["Kernel_Name"]
+    return None
 
 
 def calibrated_bytes(outdir, name, counter):
@@ -92,6 +116,61 @@ def calibrated_bytes(outdir, name, counter):
     return statistics.median(kern), factor
 
 
+class ClockSampler:
+    """Samples the shader clock with rocm-smi from a thread of this (GPU-free) process:
+    a list of (wall-clock time, MHz)."""
+
+    def __init__(self):
+        sys.path.insert(0, ROOT)
+        import bench  # noqa: E402  (the CSV parser; imports no GPU code)
+        self._parse = bench.sclk_from_csv
+        self._exe = shutil.which("rocm-smi")
+        self._stop = threading.Event()
+        self.samples = []
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    def _loop(self):
+        while self._exe and not self._stop.is_set():
+            t0 = time.time()
+            try:
+                r = subprocess.run([self._exe, "--showclocks", "--csv"], capture_output=True,
+                                   text=True, timeout=20)
+            except (OSError, subprocess.SubprocessError):
+                return
+            mhz = self._parse(r.stdout)
+            if mhz:
+                self.samples.append(((t0 + time.time()) / 2, mhz))
+            self._stop.wait(0.05)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=30)
+
+    def median_between(self, t0, t1):
+        inside = sorted(m for t, m in self.samples if t0 <= t <= t1)
+        return (inside[len(inside) // 2], len(inside)) if inside else (None, 0)
+
+
+def _timed_region(log):
+    """Wall-clock bounds of bench.py's timed region, from its stderr."""
+    with open(log) as f:
+        for line in f:
+            if line.startswith("[bench] timed region epoch"):
+                a, b = line.split()[-2:]
+                return float(a), float(b)
+    return None
+
+
+def _bench_line(path):
+    with open(path) as f:
+        lines = [x for x in f.read().splitlines() if x.startswith("{")]
+    return json.loads(lines[-1]) if lines else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="gqa16k_d256",
@@ -99,9 +178,16 @@ def main():
                          "each into its own subdirectory of --outdir)")
     ap.add_argument("--outdir", default="rocprof_out")
     ap.add_argument("--traffic-json", default=None)
-    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--md", default=None, help="write the markdown summary here")
+    ap.add_argument("--md-dir", default=None,
+                    help="write each workload's summary to <md-dir>/<kernel>__<workload>.md")
+    ap.add_argument("--steps", type=int, default=3, help="timed launches of the counter passes")
+    ap.add_argument("--trace-steps", type=int, default=100,
+                    help="timed launches of the trace pass (bench.py's default)")
+    ap.add_argument("--trace-warmup", type=int, default=5)
     ap.add_argument("--kill-after", type=int, default=90)
     a = ap.parse_args()
+    a.command = "python -m flash_attention_amd.rocprof_harness " + " ".join(sys.argv[1:])
     if a.workload != "all":
         return profile(a.workload, os.path.abspath(a.outdir), a)
     sys.path.insert(0, ROOT)
@@ -124,9 +210,16 @@ def profile(workload, out, a):
     def ok(rc):
         return rc in (0, 139)
 
+    trace_cmd = ([rp, "--kernel-trace", "--stats", "-f", "csv", "-d", os.path.join(out, "trace"),
+                  "-o", "k", "--"] +
+                 _bench_cmd(a.workload, a.trace_steps, a.trace_warmup, False))
+    with ClockSampler() as clock:
+        rc = _run(trace_cmd, os.path.join(out, "trace.log"), 300,
+                  out=os.path.join(out, "trace_bench.json"))
+    if not ok(rc):
+        print("[harness] pass trace failed (exit %d); stopping" % rc, flush=True)
+        return rc
     passes = [
-        ("trace", [rp, "--kernel-trace", "--stats", "-f", "csv", "-d", os.path.join(out, "trace"),
-                   "-o", "k", "--"] + _bench_cmd(a.workload, a.steps, 1, False), 300),
         ("util", [rp, "--pmc", "MfmaUtil", "LdsBankConflict", "-f", "csv", "-d",
                   os.path.join(out, "util"), "-o", "p", "--"] +
          _bench_cmd(a.workload, a.steps, 1, False), a.kill_after),
@@ -141,7 +234,18 @@ def profile(workload, out, a):
             print("[harness] pass %s failed (exit %d); stopping" % (name, rc), flush=True)
             return rc
 
+    # trace pass: the timed launches are the attention kernel's launches W .. W+K-1 (one
+    # per step; a split step also launches the merge once)
     dur = kernel_durations(out)
+    mdur = kernel_durations(out, MERGE_TAG)
+    W, K = a.trace_warmup, a.trace_steps
+    timed = dur[W:W + K]
+    mtimed = mdur[W:W + K]
+    line = _bench_line(os.path.join(out, "trace_bench.json"))
+    region = _timed_region(os.path.join(out, "trace.log"))
+    sclk, nsamp = clock.median_between(*region) if region else (None, 0)
+    avg_ns = statistics.mean(timed)
+    merge_ns = statistics.mean(mtimed) if mtimed else 0.0
     util = [v for k, v in counters(out, "util").values() if KERNEL_TAG in k]
     mfma = statistics.median(v["MfmaUtil"] for v in util)
     lds = statistics.median(v["LdsBankConflict"] for v in util)
@@ -149,27 +253,49 @@ def profile(workload, out, a):
     write_kib, wfac = calibrated_bytes(out, "write", "WRITE_SIZE")
     fetch_b = fetch_kib * 1024 * ffac
     write_b = write_kib * 1024 * wfac
-    avg_ns = statistics.mean(dur)
     gbs = (fetch_b + write_b) / avg_ns
     sys.path.insert(0, ROOT)
     import bench  # noqa: E402  (source hash of the kernel; imports no GPU code)
-    sha = bench.kernel_source_hash()
+    import attn_inputs  # noqa: E402
+    w = attn_inputs.WORKLOADS[a.workload]
+    roof = line["roofline"] if line else None
+    step_ns = avg_ns + merge_ns
+    # the bench line's roofline recomputed from the trace's timed launches (attention +
+    # merge per step, as the bench line's events bracket both)
+    frac_trace = None
+    if roof:
+        if roof["unit"] == "TFLOP/s":
+            frac_trace = roof["algorithmic_flops_per_launch"] / step_ns * 1e-3 / roof["peak"]
+        else:
+            frac_trace = roof["algorithmic_bytes_per_launch"] / step_ns / roof["peak"]
     summary = {
-        "kernel_sha": sha, "launches_traced": len(dur), "kernel_avg_ms": avg_ns / 1e6,
-        "kernel_min_ms": min(dur) / 1e6, "mfma_util_pct": mfma,
-        "lds_bank_conflicts_per_access": lds,
+        "kernel_sha": bench.kernel_source_hash(), "launches_traced": len(dur),
+        "timed_launches": len(timed), "kernel_avg_ms": avg_ns / 1e6,
+        "kernel_min_ms": min(timed) / 1e6, "kernel_max_ms": max(timed) / 1e6,
+        "merge_avg_ms": merge_ns / 1e6 if mtimed else None,
+        "warmup_ms": [round(x / 1e6, 4) for x in dur[:W]],
+        "sclk_mhz_timed_region": sclk, "sclk_samples": nsamp,
+        "bench_kernel_ms_mean": line.get("kernel_ms_mean") if line else None,
+        "bench_value": line.get("value") if line else None,
+        "bench_frac": roof["frac"] if roof else None, "trace_frac": frac_trace,
+        "mfma_util_pct": mfma, "lds_bank_conflicts_per_access": lds,
         "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
         "fetch_calibration": ffac, "write_calibration": wfac,
         "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
         "bytes_per_launch": fetch_b + write_b, "hbm_gbs": gbs,
+        "algorithmic_read_bytes":
+            bench.algorithmic_bytes(w) - w.B * w.Hq * w.Lq * (2 * w.D + 4),
     }
     print(json.dumps(summary, indent=1))
-    print()
-    print("| workload | kernel avg ms | MFMA util % | LDS conflicts/access | HBM read MB | "
-          "HBM write MB | HBM GB/s |")
-    print("|---|---|---|---|---|---|---|")
-    print("| %s | %.3f | %.1f | %.4f | %.1f | %.1f | %.1f |" % (
-        a.workload, avg_ns / 1e6, mfma, lds, fetch_b / 1e6, write_b / 1e6, gbs))
+    md = markdown(a, w, summary, line, kernel_name(out), trace_cmd)
+    print(md)
+    path = a.md
+    if path is None and a.md_dir:
+        short = line["config"]["kernel"] if line else "attn_fwd"
+        path = os.path.join(a.md_dir, "%s__%s.md" % (short, a.workload))
+    if path:
+        with open(path, "w") as f:
+            f.write(md)
     if a.traffic_json:
         try:
             with open(a.traffic_json) as f:
@@ -181,6 +307,71 @@ def profile(workload, out, a):
             json.dump(t, f, indent=1, sort_keys=True)
             f.write("\n")
     return 0
+
+
+def markdown(a, w, s, line, kname, trace_cmd):
+    """The summary of one workload, with the commands that made it."""
+    rel = [os.path.relpath(x, ROOT) if x.startswith(ROOT) else x for x in trace_cmd]
+    rel = ["python3" if x == sys.executable else x for x in rel]
+    frac = s["bench_frac"]
+    unit = line["roofline"]["unit"] if line else ""
+    out = []
+    out.append("# %s: %s (%s)" % (line["config"]["kernel"] if line else "attn_fwd", a.workload,
+                                  w.describe() if hasattr(w, "describe") else a.workload))
+    out.append("")
+    out.append("Made by (repository root on the MI355X box; every pass is a child process, "
+               "run from /tmp with TMPDIR=/tmp):")
+    out.append("")
+    out.append("    " + a.command)
+    out.append("")
+    out.append("Trace pass (the bench line below is this same process's output):")
+    out.append("")
+    out.append("    " + " ".join(rel))
+    out.append("")
+    out.append("Kernel source hash: `%s`.  Kernel: `%s`." % (s["kernel_sha"], kname))
+    out.append("")
+    out.append("| figure | value |")
+    out.append("|---|---|")
+    out.append("| attention launches traced | %d (%d warm-up, %d timed, then bench.py's "
+               "one-by-one launches) |" % (s["launches_traced"], len(s["warmup_ms"]),
+                                          s["timed_launches"]))
+    out.append("| warm-up launches, ms | %s |" % ", ".join("%.4f" % x for x in s["warmup_ms"]))
+    out.append("| **timed launches, trace average ms** | **%.4f** (min %.4f, max %.4f) |" % (
+        s["kernel_avg_ms"], s["kernel_min_ms"], s["kernel_max_ms"]))
+    if s["merge_avg_ms"] is not None:
+        out.append("| merge launches (timed steps), trace average ms | %.4f |" %
+                   s["merge_avg_ms"])
+    out.append("| bench line `kernel_ms_mean` (HIP events over the same timed steps) | %s |" %
+               s["bench_kernel_ms_mean"])
+    if line:
+        out.append("| bench line `value` | %s %s (`ms_per_step` %s) |" % (
+            line["value"], line["unit"], line["ms_per_step"]))
+        out.append("| bench line `roofline.frac` (%s) | %s |" % (unit, frac))
+    if s["trace_frac"] is not None:
+        out.append("| the same fraction from the trace's timed launches | %.4f |" %
+                   s["trace_frac"])
+    out.append("| shader clock in the timed region (rocm-smi, median) | %s MHz (%d samples) |"
+               % (s["sclk_mhz_timed_region"], s["sclk_samples"]))
+    out.append("| MFMA busy, %% of cycles (MfmaUtil) | %.1f |" % s["mfma_util_pct"])
+    out.append("| LDS bank conflicts per access | %.4f |" % s["lds_bank_conflicts_per_access"])
+    out.append("| HBM read per launch, MB (FETCH_SIZE x %.3f) | %.1f (%.2f x the algorithmic "
+               "Q + K + V) |" % (s["fetch_calibration"], s["fetch_bytes_per_launch"] / 1e6,
+                                 s["fetch_bytes_per_launch"] / s["algorithmic_read_bytes"]))
+    out.append("| HBM write per launch, MB (WRITE_SIZE x %.3f) | %.1f |" % (
+        s["write_calibration"], s["write_bytes_per_launch"] / 1e6))
+    out.append("")
+    out.append("Counter passes: `rocprofv3 --pmc MfmaUtil LdsBankConflict`, `--pmc FETCH_SIZE`, "
+               "`--pmc WRITE_SIZE`, each of `bench.py --workload %s --steps %d --warmup 1 "
+               "--no-cpu --no-clock` (the last two with `--copy-calib-mib %d`: a plain device "
+               "copy of known size calibrates the counter); medians over the attention "
+               "launches." % (a.workload, a.steps, COPY_MIB))
+    if line:
+        out.append("")
+        out.append("Bench line of the trace pass:")
+        out.append("")
+        out.append("    " + json.dumps(line))
+    out.append("")
+    return "\n".join(out)
 
 
 if __name__ == "__main__":
