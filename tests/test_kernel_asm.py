@@ -6,7 +6,8 @@ The kernels rely on invariants the compiler cannot enforce by itself:
 * M0 carries the LDS destination of the direct global->LDS copies, set inside the same
   inline asm statement, so the compiler must not use M0 for anything else;
 * no register spills (scratch traffic would wreck the key loop);
-* no packed fp32 VALU instructions.
+* no packed fp32 VALU instructions;
+* no scalar-memory writes (stores, atomics and write-backs go through the vector path).
 """
 import os
 import re
@@ -37,7 +38,7 @@ def asm(tmp_path_factory):
 def kernels(text, which="attn_(?:fwd|merge)_kernel"):
     """{kernel symbol: list of instruction lines with an in_asm flag}."""
     res = {}
-    pat = r"^(_Z\w*%s\w*):[^\n]*\n(.*?)^\s*s_endpgm" % which
+    pat = r"^(_Z\w*%s\w*):[^\n]*\n(.*?)^\.Lfunc_end" % which
     for m in re.finditer(pat, text, re.M | re.S):
         lines, inside = [], False
         for ln in m.group(2).splitlines():
@@ -94,6 +95,15 @@ def test_no_scratch(asm):
         assert not [ln for ln, _ in lines if ln.startswith("scratch_")], name
     for m in re.finditer(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", asm):
         assert int(m.group(1)) == 0
+
+
+def test_no_scalar_memory_writes(asm):
+    """Stores go through the vector memory path only: no scalar-cache stores, atomics or
+    write-backs (the split-merge counters use global_atomic_* instructions)."""
+    pat = re.compile(r"s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb)")
+    for name, lines in kernels(asm).items():
+        assert not [ln for ln, _ in lines if pat.match(ln)], name
+    assert not pat.search("\n".join(ln for ls in kernels(asm).values() for ln, _ in ls))
 
 
 def test_no_packed_fp32(asm):
