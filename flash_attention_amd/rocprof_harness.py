@@ -97,6 +97,17 @@ def kernel_durations(outdir, tag=KERNEL_TAG):
     return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
 
 
+def kernel_stats(outdir):
+    """Rows of rocprofv3's --stats summary (k_kernel_stats.csv) for the attention and
+    merge kernels: (name, calls, average ns, min ns, max ns)."""
+    rows = []
+    for r in _rows(os.path.join(outdir, "trace", "**", "*kernel_stats.csv")):
+        if KERNEL_TAG in r["Name"] or MERGE_TAG in r["Name"]:
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]),
+                         float(r["MinNs"]), float(r["MaxNs"])))
+    return rows
+
+
 def kernel_name(outdir, tag=KERNEL_TAG):
     for r in _rows(os.path.join(outdir, "trace", "**", "*kernel_trace.csv")):
         if tag in r["Kernel_Name"]:
@@ -186,8 +197,20 @@ def main():
                     help="timed launches of the trace pass (bench.py's default)")
     ap.add_argument("--trace-warmup", type=int, default=5)
     ap.add_argument("--kill-after", type=int, default=90)
+    ap.add_argument("--index", default=None,
+                    help="only write a table of every workload in this --traffic-json file "
+                         "(to --md) and exit")
     a = ap.parse_args()
-    a.command = "python -m flash_attention_amd.rocprof_harness " + " ".join(sys.argv[1:])
+    # (paths inside the repository are shown relative to its root)
+    a.command = "python -m flash_attention_amd.rocprof_harness " + " ".join(
+        os.path.relpath(x, ROOT) if x.startswith(ROOT + os.sep) else x for x in sys.argv[1:])
+    if a.index:
+        text = index_table(a.index, a.command)
+        print(text)
+        if a.md:
+            with open(a.md, "w") as f:
+                f.write(text)
+        return 0
     if a.workload != "all":
         return profile(a.workload, os.path.abspath(a.outdir), a)
     sys.path.insert(0, ROOT)
@@ -287,6 +310,7 @@ def profile(workload, out, a):
             bench.algorithmic_bytes(w) - w.B * w.Hq * w.Lq * (2 * w.D + 4),
     }
     print(json.dumps(summary, indent=1))
+    summary["stats"] = kernel_stats(out)
     md = markdown(a, w, summary, line, kernel_name(out), trace_cmd)
     print(md)
     path = a.md
@@ -307,6 +331,35 @@ def profile(workload, out, a):
             json.dump(t, f, indent=1, sort_keys=True)
             f.write("\n")
     return 0
+
+
+def index_table(traffic_json, command):
+    """One line per workload of a --traffic-json file (what each per-workload summary
+    holds, side by side)."""
+    with open(traffic_json) as f:
+        t = json.load(f)
+    out = ["# rocprofv3 summaries of every workload (attention kernel)", "",
+           "Made by (repository root):", "", "    " + command, "",
+           "from the figures each workload's own summary records (its trace pass: W warm-up "
+           "and K timed launches beside the bench line of the same process; its counter "
+           "passes: MfmaUtil and LdsBankConflict, FETCH_SIZE, WRITE_SIZE, each calibrated "
+           "by a plain device copy of known size).", "",
+           "| workload | kernel source hash | timed launches | trace average ms | bench "
+           "`roofline.frac` | same from the trace | shader clock MHz | MFMA busy % | "
+           "LDS conflicts / access | HBM read MB (x algorithmic) | HBM write MB |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name in sorted(t):
+        s = t[name]
+        if "trace_frac" not in s:
+            continue
+        out.append("| %s | %s | %d | %.4f | %s | %.4f | %s | %.1f | %.4f | %.1f (%.2f) | %.1f |" % (
+            name, s["kernel_sha"], s["timed_launches"], s["kernel_avg_ms"], s["bench_frac"],
+            s["trace_frac"], s["sclk_mhz_timed_region"], s["mfma_util_pct"],
+            s["lds_bank_conflicts_per_access"], s["fetch_bytes_per_launch"] / 1e6,
+            s["fetch_bytes_per_launch"] / s["algorithmic_read_bytes"],
+            s["write_bytes_per_launch"] / 1e6))
+    out.append("")
+    return "\n".join(out)
 
 
 def markdown(a, w, s, line, kname, trace_cmd):
@@ -359,6 +412,17 @@ def markdown(a, w, s, line, kname, trace_cmd):
                                  s["fetch_bytes_per_launch"] / s["algorithmic_read_bytes"]))
     out.append("| HBM write per launch, MB (WRITE_SIZE x %.3f) | %.1f |" % (
         s["write_calibration"], s["write_bytes_per_launch"] / 1e6))
+    if s.get("stats"):
+        out.append("")
+        out.append("rocprofv3 `--stats` summary of the trace pass (`k_kernel_stats.csv`: every "
+                   "launch of the run, the warm-up and bench.py's one-by-one launches after the "
+                   "timed region included; the timed-launch average above is taken from the "
+                   "same run's `k_kernel_trace.csv`):")
+        out.append("")
+        out.append("| kernel | calls | average ns | min ns | max ns |")
+        out.append("|---|---|---|---|---|")
+        for name, calls, avg, lo, hi in s["stats"]:
+            out.append("| `%s` | %d | %.0f | %.0f | %.0f |" % (name[:90], calls, avg, lo, hi))
     out.append("")
     out.append("Counter passes: `rocprofv3 --pmc MfmaUtil LdsBankConflict`, `--pmc FETCH_SIZE`, "
                "`--pmc WRITE_SIZE`, each of `bench.py --workload %s --steps %d --warmup 1 "

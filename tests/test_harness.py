@@ -78,3 +78,24 @@ def test_markdown_names_commands():
     assert "python -m x --workload y" in md
     assert "rocprofv3 --kernel-trace -- python3 bench.py" in md
     assert "1880 MHz" in md and "2.00 x" in md
+
+
+def test_kernel_stats_and_index(tmp_path):
+    d = str(tmp_path)
+    os.makedirs(os.path.join(d, "trace", "h"))
+    with open(os.path.join(d, "trace", "h", "k_kernel_stats.csv"), "w") as f:
+        f.write("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs,StdDev\n")
+        f.write('"attn_fwd_kernel<x>",10,100,10.0,90,9,11,0.5\n')
+        f.write('"__amd_rocclr_copyBuffer",3,30,10.0,10,9,11,0.5\n')
+    assert rh.kernel_stats(d) == [("attn_fwd_kernel<x>", 10, 10.0, 9.0, 11.0)]
+    t = {"w1": {"kernel_sha": "abc", "timed_launches": 100, "kernel_avg_ms": 7.0,
+                "bench_frac": 0.5, "trace_frac": 0.5, "sclk_mhz_timed_region": 1800,
+                "mfma_util_pct": 63.0, "lds_bank_conflicts_per_access": 0.0,
+                "fetch_bytes_per_launch": 6e8, "algorithmic_read_bytes": 3e8,
+                "write_bytes_per_launch": 2e8},
+         "old": {"kernel_sha": "x", "bytes_per_launch": 1}}
+    p = tmp_path / "t.json"
+    p.write_text(json.dumps(t))
+    text = rh.index_table(str(p), "python -m x")
+    assert "| w1 | abc | 100 | 7.0000 | 0.5 | 0.5000 | 1800 | 63.0 | 0.0000 | 600.0 (2.00) | 200.0 |" in text
+    assert "| old |" not in text
