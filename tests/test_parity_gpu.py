@@ -300,6 +300,25 @@ def test_reference_growth_last_tile_and_repeated():
     parity(q, k, v, scale_of(D), "f16", what="growth repeated")
 
 
+@pytest.mark.parametrize("D,dt", [(256, "f16"), (128, "bf16")])
+def test_reference_growth_in_one_block_only(D, dt):
+    """Growth confined to one 32-row query block: every query row is made orthogonal to a
+    unit vector u, then rows 32..63 of head 0 get 2u added, and key 333 is 250u.  Only those
+    rows see the large score (block 1 of the first wavefront at D=256, the second wavefront
+    at D=128), so only that block rescales; every other row keeps its first-tile reference."""
+    _announce("growth in one block D=%d %s" % (D, dt))
+    q, k, v = attn_inputs.make_qkv(1, 2, 1, 256, 700, D, dt, seed=25)
+    g = torch.Generator().manual_seed(125)
+    u = torch.randn(D, generator=g, dtype=torch.float64)
+    u = u / u.norm()
+    qd = q.double()
+    qd = qd - (qd @ u)[..., None] * u
+    qd[0, 0, 32:64] += 2.0 * u
+    q = qd.to(q.dtype)
+    k[0, 0, 333] = (u * 250.0).to(k.dtype)
+    parity(q, k, v, scale_of(D), dt, what="growth in one block")
+
+
 @pytest.mark.parametrize("D,dt", [(128, "f16"), (128, "bf16"), (256, "f16")])
 @pytest.mark.parametrize("causal,nsplit", [(False, 3), (True, 1), (True, 2)])
 def test_reference_growth_with_mask_and_splits(D, dt, causal, nsplit):
