@@ -347,17 +347,44 @@ def test_plan_ex_split_choice(shape, expect):
     assert base.nsplit == 1 and base.workspace_bytes == 0
 
 
-def test_planner_narrow_shape_only_for_split_groups_up_to_256_rows():
-    # 256-row groups that need splits: narrow (with 64 batch entries the narrow shape fills
-    # the GPU with no split at all, rather than the wide one with partials); the same groups
-    # with enough work unsplit, and groups past 256 rows: wide; explicit plans (attn_plan)
-    # keep the default shape
+def test_planner_weighs_the_narrow_shape_for_split_groups():
+    # groups that need splits: narrow (with 64 batch entries the narrow shape fills the GPU
+    # with no split at all, rather than the wide one with partials); the same groups with
+    # enough work unsplit: wide; explicit plans (attn_plan) keep the default shape
     assert fa.attn_plan_ex(4, 32, 2, 16, 16384, 256, fa.ATTN_F16, 1).block_m == 128
     p = fa.attn_plan_ex(64, 32, 2, 16, 4096, 256, fa.ATTN_F16, 0)
     assert (p.block_m, p.nsplit) == (128, 1)
     assert fa.attn_plan_ex(256, 32, 2, 16, 4096, 256, fa.ATTN_F16, 0).block_m == 256
-    assert fa.attn_plan_ex(1, 32, 2, 17, 16384, 256, fa.ATTN_F16, 0).block_m == 256
     assert fa.attn_plan(4, 32, 2, 16, 16384, 256, fa.ATTN_F16).block_m == 256
+    # past 256 rows too: 272 rows (a ragged second wide tile) and 512 rows with few groups
+    assert fa.attn_plan_ex(1, 32, 2, 17, 16384, 256, fa.ATTN_F16, 0).block_m == 128
+    assert fa.attn_plan_ex(2, 16, 2, 64, 8192, 256, fa.ATTN_F16, 0).block_m == 128
+
+
+# Planner picks on the shapes of a measured sweep (one MI355X; every split count of both tile
+# shapes timed, attention and merge launches together): the plan the planner picks, and the
+# fastest measured plans it has to be among (those within 1 % of the fastest, or a split count
+# between two of them).  B, Hq, Hkv, Lq, Lk, D, dtype, causal -> (rows per workgroup,
+# smallest and largest acceptable split count).
+MEASURED_BEST = [
+    ((4, 32, 2, 16, 16384, 256, fa.ATTN_F16, 1), (128, 16, 16)),    # 52.9 us at 16 splits
+    ((1, 32, 8, 1, 65536, 128, fa.ATTN_BF16, 1), (128, 64, 64)),    # 46.7 us at 64
+    ((1, 32, 2, 1024, 16384, 256, fa.ATTN_F16, 0), (256, 2, 2)),    # 473.6 us at 2
+    ((1, 32, 8, 4, 32768, 128, fa.ATTN_F16, 1), (128, 64, 64)),     # 28.3 us at 64 (best 28.1)
+    ((2, 16, 2, 64, 8192, 256, fa.ATTN_F16, 0), (128, 12, 16)),     # 36.5 / 36.8 us at 12 / 16
+    ((8, 32, 8, 1, 8192, 128, fa.ATTN_BF16, 1), (128, 8, 8)),       # 46.0 us at 8
+    ((1, 32, 4, 256, 32768, 128, fa.ATTN_F16, 0), (256, 8, 8)),     # 142.5 us at 8
+    ((1, 64, 8, 128, 16384, 256, fa.ATTN_F16, 0), (256, 8, 8)),     # 139.6 us at 8
+    ((16, 32, 8, 2, 4096, 128, fa.ATTN_F16, 1), (128, 4, 4)),       # 46.0 us at 4
+    ((1, 8, 1, 2048, 65536, 128, fa.ATTN_F16, 0), (256, 4, 4)),     # 511.0 us at 4
+]
+
+
+@pytest.mark.parametrize("shape,expect", MEASURED_BEST)
+def test_planner_matches_measured_best(shape, expect):
+    B, Hq, Hkv, Lq, Lk, D, dt, causal = shape
+    p = fa.attn_plan_ex(B, Hq, Hkv, Lq, Lk, D, dt, fa.ATTN_CAUSAL if causal else 0)
+    assert p.block_m == expect[0] and expect[1] <= p.nsplit <= expect[2], (p.block_m, p.nsplit)
 
 
 def test_plan_ex_names_the_causal_kernel():
