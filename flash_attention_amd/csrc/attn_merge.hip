@@ -13,13 +13,15 @@
 // Memory-bound: every partial element is read once and every output element written once.
 // One thread owns 4 consecutive elements of one row (one 16-byte load per part, one 8- or
 // 16-byte store), so a wavefront reads 1 KiB of contiguous bytes per part, with the loads
-// of four parts issued together.  When there are few rows (decode-sized queries split over
-// many key ranges) one wavefront per 64 output chunks would walk all parts one batch after
-// another on a handful of compute units; then the parts are dealt to the PG wavefronts of
-// a workgroup (part s to wavefront s % PG).  Each wavefront weighs its parts against the
-// largest LSE among them; the PG partial sums meet in LDS, rescaled to the common maximum
-// and added in a fixed order, so the result does not depend on timing.  The row's LSE
-// values are read by all of its threads (the same cache lines).
+// of four parts (and their LSE values) issued together, in one pass: the running sums are
+// rescaled to a new largest LSE when a batch brings one (a separate pass for the maximum
+// first would cost another round trip to memory).  When there are few rows (decode-sized
+// queries split over many key ranges) one wavefront per 64 output chunks would walk all
+// parts one batch after another on a handful of compute units; then the parts are dealt to
+// the PG wavefronts of a workgroup (part s to wavefront s % PG).  Each wavefront weighs its
+// parts against the largest LSE among them; the PG partial sums meet in LDS, rescaled to
+// the common maximum and added in a fixed order, so the result does not depend on timing.
+// The row's LSE values are read by all of its threads (the same cache lines).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -60,40 +62,41 @@ __global__ __launch_bounds__(64 * PG) void attn_merge_kernel(MergeParams p) {
   const int col = static_cast<int>(chunk - row * cpr) * kVec;
   const float* lse_row = p.lse_part + row;  // part s at lse_row[s * rows]
 
-  // The largest LSE among this wavefront's parts (all parts when PG = 1); the PG partial
-  // sums, each relative to its own maximum, are rescaled to the common one when they meet.
-  float top = -__builtin_inff();
-  if (live)
-    for (int s = wave; s < p.nparts; s += PG) top = fmaxf(top, lse_row[s * p.rows]);
-
-  // weights relative to the largest part: exp(LSE_s - top) <= 1 (0 for an empty part),
-  // their sum >= 1; the partial outputs are summed unnormalised and scaled once
+  // One pass over this wavefront's parts, kBatch at a time with all their loads issued
+  // together; the running sums are rescaled when a batch raises the largest LSE.
   constexpr float kLog2e = 1.4426950408889634f;
+  float top = -__builtin_inff();
   f32x4 acc = {0, 0, 0, 0};
   float sum = 0.f;
-  if (live && top != -__builtin_inff()) {
+  if (live) {
     const float* src = p.o_part + row * p.D + col;
     const int64_t step = p.rows * p.D;  // one part
-    int s = wave;
-    for (; s + (kBatch - 1) * PG < p.nparts; s += kBatch * PG) {
+    for (int s0 = wave; s0 < p.nparts; s0 += kBatch * PG) {
       f32x4 x[kBatch];
-      float w[kBatch];
+      float lv[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        x[j] = *reinterpret_cast<const f32x4*>(src + (s + j * PG) * step);
-        w[j] = __builtin_amdgcn_exp2f((lse_row[(s + j * PG) * p.rows] - top) * kLog2e);
+        const int s = s0 + j * PG;
+        const bool have = s < p.nparts;
+        const int sc = have ? s : s0;  // (a part that exists; its weight is zeroed)
+        x[j] = *reinterpret_cast<const f32x4*>(src + sc * step);
+        const float l = lse_row[sc * p.rows];
+        lv[j] = have ? l : -__builtin_inff();
       }
+      float bt = top;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) bt = fmaxf(bt, lv[j]);
+      if (bt == -__builtin_inff()) continue;
+      const float f = __builtin_amdgcn_exp2f((top - bt) * kLog2e);
+      acc *= f;
+      sum *= f;
+      top = bt;
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        // an empty part (weight 0) must not bring in its output (not required finite)
-        if (w[j] != 0.f) acc += w[j] * x[j];
-        sum += w[j];
+        const float w = __builtin_amdgcn_exp2f((lv[j] - top) * kLog2e);
+        if (w != 0.f) acc += w * x[j];
+        sum += w;
       }
-    }
-    for (; s < p.nparts; s += PG) {
-      const float w = __builtin_amdgcn_exp2f((lse_row[s * p.rows] - top) * kLog2e);
-      if (w != 0.f) acc += w * *reinterpret_cast<const f32x4*>(src + s * step);
-      sum += w;
     }
   }
   if constexpr (PG > 1) {
