@@ -196,6 +196,35 @@ def test_merge_many_parts_few_rows(P, rows, D):
     assert np.abs(lg[fin] - lse_ref[fin]).max() <= 1e-5 * 20
 
 
+@pytest.mark.parametrize("P,rows,order", [(16, 2048, "rising"), (16, 2048, "falling"),
+                                          (64, 32, "rising"), (7, 513, "last_dominates")])
+def test_merge_rescales_across_batches(P, rows, order):
+    """The merge takes the parts in batches and rescales its running sums whenever a batch
+    brings a larger LSE: LSE rising part by part (every batch rescales), falling (none
+    does), and the last part of every row 120 above all others (once it arrives, the
+    others' weights exp(-120) underflow to 0 in fp32): against the oracle's merge."""
+    _announce("merge rescale P=%d rows=%d %s" % (P, rows, order))
+    g = torch.Generator().manual_seed(29 + P)
+    o_part = torch.randn(P, rows, 256, generator=g)
+    base = torch.rand(P, rows, generator=g) * 2
+    steps = torch.arange(P, dtype=torch.float32)[:, None] * 3.0
+    if order == "rising":
+        lse_part = base + steps
+    elif order == "falling":
+        lse_part = base - steps
+    else:
+        lse_part = base.clone()
+        lse_part[P - 1] += 120.0
+    dev = torch.device("cuda:0")
+    o, lse = fa.merge(o_part.to(dev), lse_part.to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.merge(o_part.double().numpy(), lse_part.double().numpy())
+    og, lg = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    assert np.abs(og - o_ref).max() <= 2e-6 * max(1.0, np.abs(o_ref).max())
+    assert np.abs(lg - lse_ref).max() <= 1e-5 * max(1.0, np.abs(lse_ref).max())
+
+
 def test_merge_without_lse_and_single_part():
     """lse = NULL leaves no LSE; one part merges to itself (weight exactly 1)."""
     _announce("merge single part")
