@@ -20,12 +20,13 @@ struct Tile;
 // as large; with two wavefronts per SIMD the hardware issues one's exponentials while the
 // other's MFMAs run.  One query block keeps a wavefront within half the register file
 // (64 accumulator + ~150 other registers).
+// Six K/V stages (96 KiB): copies two tiles ahead and one workgroup barrier per two tiles.
 template <>
 struct Tile<128, 0> {
   static constexpr int WAVES = 8;   // wavefronts per workgroup
   static constexpr int QB = 1;      // 32-row query blocks per wavefront
   static constexpr int BN = 32;     // keys per LDS tile
-  static constexpr int STAGES = 4;  // K/V tiles resident in LDS at once
+  static constexpr int STAGES = 6;  // K/V tiles resident in LDS at once
   static constexpr int WG_PER_CU = 1;  // workgroups per compute unit (registers, LDS)
 };
 

@@ -220,6 +220,19 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t
                : "memory");
 }
 
+// f(std::integral_constant<int, I>{}, t + I - I0) for I = I0 .. N-1 in order while
+// t + I - I0 < n; the first t not done.
+template <int I, int N, typename F>
+__device__ __forceinline__ int unroll_steps(int t, int n, F&& f) {
+  if constexpr (I < N) {
+    if (t >= n) return t;
+    f(std::integral_constant<int, I>{}, t);
+    return unroll_steps<I + 1, N>(t + 1, n, static_cast<F&&>(f));
+  } else {
+    return t;
+  }
+}
+
 // Growth threshold of the lazy rescale.  The exponentials use a per-row reference m: the
 // first key tile's maximum, raised only when a later tile outgrows it by this factor.  All
 // weights are non-negative, so a lane whose partial sum over a tile stays at or below the
@@ -242,7 +255,14 @@ void attn_fwd_kernel(Params p) {
                 "one 32-key block per tile");
   constexpr int THREADS = attn_cfg::threads<D, V>();
   constexpr int WAVES = attn_cfg::Tile<D, V>::WAVES;
-  static_assert(NSTAGE == 4, "tiles t-1 (V), t (K), t+1 (landing) resident; a fourth stage keeps the unrolled loop's stage offsets static");
+  // Four stages: tiles t-1 (V, and K for a rescale), t, t+1 (landing) resident, a fourth
+  // keeping the unrolled loop's stage offsets static; the copies of tile t+1 are issued in
+  // iteration t and every iteration ends at a workgroup barrier.  Six stages (HD=128 wide
+  // shape): the copies run two tiles ahead, and only odd iterations end at a barrier, which
+  // then covers the two tiles landed for the next two iterations (the barrier is a measured
+  // 4 % of that kernel's time).
+  static_assert(NSTAGE == 4 || NSTAGE == 6, "four or six stages");
+  constexpr int PF = NSTAGE == 6 ? 2 : 1;  // tiles between a tile's copies and its use
   constexpr int KS = D / 16;    // contraction steps of S^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -410,15 +430,19 @@ void attn_fwd_kernel(Params p) {
   // fragment read spread over distinct banks.  Rows past Lq re-read row Lq-1 (never
   // stored).
   constexpr int NQB = BM / 32;                           // query blocks per workgroup
-  constexpr bool Q_FILLS_LDS = NQB > 2 * NSTAGE - 2;     // tile 0 waits for Q
+  constexpr bool Q_FILLS_LDS = NQB > 2 * (NSTAGE - PF);  // the first tiles wait for Q
   constexpr int QCOPY_PER_BLOCK = TILE * 2 / 1024;       // 1 KiB copies per block
   constexpr int QCOPIES = NQB * QCOPY_PER_BLOCK / WAVES;  // per wave
   static_assert(NQB <= 2 * NSTAGE && QCOPIES * WAVES == NQB * QCOPY_PER_BLOCK,
                 "Q fits the stage slots, in whole copies per wave");
-  auto qslot = [](int b) { return Q_FILLS_LDS ? b : b + 1 + (b >= NSTAGE - 1); };
+  // (the slots of tiles 0 .. PF-1 are K stages 0 .. PF-1 and V stages 0 .. PF-1)
+  auto qslot = [](int b) { return Q_FILLS_LDS ? b : b < NSTAGE - PF ? b + PF : b + 2 * PF; };
   {
     const i32x4 qrsrc = make_rsrc(qh, static_cast<uint32_t>(p.Lq) * D * 2);
-    if (!Q_FILLS_LDS && ntiles > 0) issue_tile(0, 0);
+    if (!Q_FILLS_LDS && ntiles > 0) {
+#pragma unroll
+      for (int t0 = 0; t0 < PF; ++t0) issue_tile(t0, t0);
+    }
 #pragma unroll
     for (int j = 0; j < QCOPIES; ++j) {
       const int n = wave + WAVES * j;
@@ -443,8 +467,11 @@ void attn_fwd_kernel(Params p) {
       qf[qb][kk] = *reinterpret_cast<const u32x4*>(qs + 16 * ((2 * kk + hi) ^ (l32 % CPR)));
   }
   if constexpr (Q_FILLS_LDS) {
-    __syncthreads();  // every wave has its Q: the slots take tile 0
-    if (ntiles > 0) issue_tile(0, 0);
+    __syncthreads();  // every wave has its Q: the slots take the first tiles
+    if (ntiles > 0) {
+#pragma unroll
+      for (int t0 = 0; t0 < PF; ++t0) issue_tile(t0, t0);
+    }
   }
 
   // ---- per-lane LDS byte offsets of the fragment reads (stage base added later) ----
@@ -693,12 +720,16 @@ void attn_fwd_kernel(Params p) {
     }
   };
 
-  // Synchronisation point at the end of iteration t: tile t+1 (copied under this
-  // iteration's S^T MFMAs) has landed everywhere, and every wave is done with the V of tile
-  // t-1, so the next iteration may read tile t+1 and copy tile t+2 into the stage of tile
-  // t-2.
+  // Synchronisation point at the end of iteration t.  Four stages (every iteration): tile
+  // t+1 (copied under this iteration's S^T MFMAs) has landed everywhere, and every wave is
+  // done with tile t-1, so the next iteration may read tile t+1 and copy tile t+2 into the
+  // stage of tile t-2.  Six stages (odd t only): tiles t+1 and t+2 (copied in iterations t-1
+  // and t) have landed everywhere and every wave is done with iteration t, so the next two
+  // iterations may read them and copy tiles t+3 and t+4 into the stages of tiles t-3 and
+  // t-2; between barriers a wave is at most one iteration ahead of another, and the stages
+  // one iteration reads (t, t-1) are never the ones the other copies into.
   auto sync_point = [&](int t) {
-    if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of tile t+1
+    if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of the tiles to come
     // A bare s_barrier: every LDS read of this iteration has been waited for by the MFMA
     // that consumed it.
     __builtin_amdgcn_s_barrier();
@@ -716,8 +747,8 @@ void attn_fwd_kernel(Params p) {
     constexpr int VST = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
     u32x4 vf[3];
     // S^T(t); under its MFMAs the weights of tile t-1 are packed, and the copies of tile
-    // t+1 issued into the stage of tile t-3 (free: every wave is past iteration t-1's
-    // barrier), copy j after MFMA j*W/NCOPY
+    // t+PF issued into the stage of tile t+PF-NSTAGE (t-3, or t-4 with six stages: free,
+    // every wave is past the iteration that last read it), copy j after MFMA j*W/NCOPY
     constexpr int W = QB * KS;  // S^T windows
     static_assert(W % NCOPY == 0, "whole S^T windows per copy");
     qk(kstage(ST), sacc, kf,
@@ -729,7 +760,7 @@ void attn_fwd_kernel(Params p) {
        },
        [&](int w) {
          if constexpr (PV) pack_slice(NPAIR * w / W, NPAIR * (w + 1) / W);
-         if (w % (W / NCOPY) == 0) issue_copy(t + 1, (ST + 1) % NSTAGE, w / (W / NCOPY));
+         if (w % (W / NCOPY) == 0) issue_copy(t + PF, (ST + PF) % NSTAGE, w / (W / NCOPY));
        });
     if constexpr (PV) {
       rescale_if_grown(t - 1, kstage(VST), kstage(ST), sacc);
@@ -765,7 +796,8 @@ void attn_fwd_kernel(Params p) {
         }
         if (h >= EXP0)
           exp_slice(sacc, NELEM * (h - EXP0) / (H - EXP0), NELEM * (h - EXP0 + 1) / (H - EXP0));
-        if (h == H - 1) sync_point(t);
+        // (six stages: odd iterations only; the stage parity is the iteration's parity)
+        if (h == H - 1 && (PF == 1 || ST % 2 == 1)) sync_point(t);
         if (h == H - 1 && t + 1 < ntiles) {
           // first two K fragments of tile t+1 (landed at the sync point)
           kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
@@ -798,30 +830,31 @@ void attn_fwd_kernel(Params p) {
   // The weights use a per-row reference m set by the first key tile instead of a maximum
   // kept up to date at every tile, so the output accumulator is rescaled only in the rare
   // tile whose scores outgrow m by more than a factor kGrowth (rescale_if_grown).  The loop
-  // is unrolled by four: the stage of each iteration is a compile-time constant.
+  // is unrolled by NSTAGE: the stage of each iteration is a compile-time constant.
   f32x16 sacc[QB];  // scores of the current tile
   // (a workgroup with no key to look at, under the causal mask or past the last split,
   // skips the loop: its rows are empty)
   if (ntiles > 0) {
-    WAIT_VMCNT(0);  // tile 0 landed
+    WAIT_VMCNT(0);  // the first tiles landed
     __syncthreads();
     kf[0] = kfrag(kstage(0), 0);
     kf[1] = kfrag(kstage(0), 1);
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
-    iteration(std::false_type{}, S0{}, 0, sacc);
+    iteration(std::false_type{}, std::integral_constant<int, 0>{}, 0, sacc);
     int t = 1;
+    // unrolled by NSTAGE: iteration t runs with stage t % NSTAGE as a compile-time constant
     while (t < ntiles) {
-      iteration(std::true_type{}, S1{}, t, sacc);
-      if (++t >= ntiles) break;
-      iteration(std::true_type{}, S2{}, t, sacc);
-      if (++t >= ntiles) break;
-      iteration(std::true_type{}, S3{}, t, sacc);
-      if (++t >= ntiles) break;
-      iteration(std::true_type{}, S0{}, t, sacc);
-      ++t;
+#define ATTN_ITER(J)                                                                   \
+  iteration(std::true_type{}, std::integral_constant<int, (1 + (J)) % NSTAGE>{}, t, sacc); \
+  if (++t >= ntiles) break;
+      ATTN_ITER(0)
+      ATTN_ITER(1)
+      ATTN_ITER(2)
+      ATTN_ITER(3)
+      if constexpr (NSTAGE == 6) {
+        ATTN_ITER(4)
+        ATTN_ITER(5)
+      }
+#undef ATTN_ITER
     }
     drain(ntiles - 1, sacc);
     // the last iteration copied (zeros) for a tile past the end: let it land before the
