@@ -27,6 +27,7 @@ struct Tile<128, 0> {
   static constexpr int QB = 1;      // 32-row query blocks per wavefront
   static constexpr int BN = 32;     // keys per LDS tile
   static constexpr int STAGES = 6;  // K/V tiles resident in LDS at once
+  static constexpr int PREFETCH = 2;  // key tiles between a tile's copies and its use
   static constexpr int WG_PER_CU = 1;  // workgroups per compute unit (registers, LDS)
 };
 
@@ -39,6 +40,7 @@ struct Tile<256, 0> {
   static constexpr int QB = 2;
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
+  static constexpr int PREFETCH = 2;
   static constexpr int WG_PER_CU = 1;
 };
 
@@ -51,6 +53,7 @@ struct Tile<128, 1> {
   static constexpr int QB = 1;
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
+  static constexpr int PREFETCH = 1;  // (two: 2.4 % slower with two workgroups per CU)
   static constexpr int WG_PER_CU = 2;
 };
 
@@ -62,6 +65,7 @@ struct Tile<256, 1> {
   static constexpr int QB = 1;
   static constexpr int BN = 32;
   static constexpr int STAGES = 4;
+  static constexpr int PREFETCH = 2;
   static constexpr int WG_PER_CU = 1;
 };
 

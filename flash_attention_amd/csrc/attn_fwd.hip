@@ -255,14 +255,17 @@ void attn_fwd_kernel(Params p) {
                 "one 32-key block per tile");
   constexpr int THREADS = attn_cfg::threads<D, V>();
   constexpr int WAVES = attn_cfg::Tile<D, V>::WAVES;
-  // Four stages: tiles t-1 (V, and K for a rescale), t, t+1 (landing) resident, a fourth
-  // keeping the unrolled loop's stage offsets static; the copies of tile t+1 are issued in
-  // iteration t and every iteration ends at a workgroup barrier.  Six stages (HD=128 wide
-  // shape): the copies run two tiles ahead, and only odd iterations end at a barrier, which
-  // then covers the two tiles landed for the next two iterations (the barrier is a measured
-  // 4 % of that kernel's time).
-  static_assert(NSTAGE == 4 || NSTAGE == 6, "four or six stages");
-  constexpr int PF = NSTAGE == 6 ? 2 : 1;  // tiles between a tile's copies and its use
+  // Four stages, every iteration ending at a workgroup barrier: tiles t-1 (V, and K for a
+  // rescale) and t are read, the copies of tile t+PF are issued in iteration t.  With PF = 1
+  // the fourth stage keeps the unrolled loop's stage offsets static; with PF = 2 it holds
+  // tile t+2 in flight while the barrier waits only for tile t+1, so a copy has one and a
+  // half iterations to land instead of a half.  Six stages (HD=128 wide shape): copies two
+  // tiles ahead, and only odd iterations end at a barrier, which then covers the two tiles
+  // landed for the next two iterations (the barrier is a measured 4 % of that kernel's
+  // time).
+  constexpr int PF = attn_cfg::Tile<D, V>::PREFETCH;  // tiles between a tile's copies and use
+  static_assert((NSTAGE == 4 && (PF == 1 || PF == 2)) || (NSTAGE == 6 && PF == 2),
+                "four stages with copies one or two tiles ahead, or six with two");
   constexpr int KS = D / 16;    // contraction steps of S^T
   constexpr int DB = D / 32;    // 32-row blocks of O^T
   constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -720,16 +723,24 @@ void attn_fwd_kernel(Params p) {
     }
   };
 
+  constexpr int NCOPY = 2 * LOADS;  // copies per thread and tile
+
   // Synchronisation point at the end of iteration t.  Four stages (every iteration): tile
-  // t+1 (copied under this iteration's S^T MFMAs) has landed everywhere, and every wave is
-  // done with tile t-1, so the next iteration may read tile t+1 and copy tile t+2 into the
-  // stage of tile t-2.  Six stages (odd t only): tiles t+1 and t+2 (copied in iterations t-1
-  // and t) have landed everywhere and every wave is done with iteration t, so the next two
-  // iterations may read them and copy tiles t+3 and t+4 into the stages of tiles t-3 and
-  // t-2; between barriers a wave is at most one iteration ahead of another, and the stages
-  // one iteration reads (t, t-1) are never the ones the other copies into.
+  // t+1 has landed everywhere (copied in iteration t, or t-1 with PF = 2, whose copies of
+  // tile t+2 may still be in flight: a wave waits until at most its own NCOPY newest copies
+  // are), and every wave is done with tile t-1, so the next iteration may read tile t+1 and
+  // copy tile t+1+PF into the stage of tile t+1+PF-4.  Six stages (odd t only): tiles t+1
+  // and t+2 (copied in iterations t-1 and t) have landed everywhere and every wave is done
+  // with iteration t, so the next two iterations may read them and copy tiles t+3 and t+4
+  // into the stages of tiles t-3 and t-2; between barriers a wave is at most one iteration
+  // ahead of another, and the stages one iteration reads (t, t-1) are never the ones the
+  // other copies into.
   auto sync_point = [&](int t) {
-    if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of the tiles to come
+    if constexpr (NSTAGE == 4 && PF == 2) {
+      WAIT_VMCNT(NCOPY);  // this thread's copies of tile t+1 (those of t+2 may fly)
+    } else {
+      if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of the tiles to come
+    }
     // A bare s_barrier: every LDS read of this iteration has been waited for by the MFMA
     // that consumed it.
     __builtin_amdgcn_s_barrier();
@@ -737,10 +748,9 @@ void attn_fwd_kernel(Params p) {
 
   // One key-loop iteration for tile t: S^T(t) = K(t) Q^T, then the P.V MFMAs of tile t-1
   // (PV) with the softmax of tile t in slices underneath.
-  constexpr int NCOPY = 2 * LOADS;  // copies per thread and tile
   u32x4 kf[3];
   constexpr int NPAIR = NELEM / 2;  // packed weight pairs per lane and tile
-  // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by four.
+  // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by NSTAGE.
   auto iteration = [&](auto pv_tag, auto st_tag, int t, f32x16 (&sacc)[QB]) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
@@ -797,7 +807,7 @@ void attn_fwd_kernel(Params p) {
         if (h >= EXP0)
           exp_slice(sacc, NELEM * (h - EXP0) / (H - EXP0), NELEM * (h - EXP0 + 1) / (H - EXP0));
         // (six stages: odd iterations only; the stage parity is the iteration's parity)
-        if (h == H - 1 && (PF == 1 || ST % 2 == 1)) sync_point(t);
+        if (h == H - 1 && (NSTAGE == 4 || ST % 2 == 1)) sync_point(t);
         if (h == H - 1 && t + 1 < ntiles) {
           // first two K fragments of tile t+1 (landed at the sync point)
           kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
