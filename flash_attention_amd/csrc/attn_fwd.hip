@@ -368,28 +368,23 @@ void attn_fwd_kernel(Params p) {
       vk[par] = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_k(par * ROWS_PER_LOAD + r0)) * 16);
     vv = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
   }
-  // Bytes of K (V) this workgroup may copy: its tiles, cut at the end of K (V).  Copies past
-  // them read zeros (the key loop issues the copies of tile t+1 without checking t+1 <
-  // ntiles, which would cost a branch per copy).
+  // Bytes of K (V) this workgroup may copy: its tiles, cut at the end of K (V).  One buffer
+  // descriptor per tensor covers them for the whole sweep (base: this workgroup's first
+  // key); a copy's byte offset at or past the size reads zeros, which fills the rows past Lk
+  // of a partial last tile, and the copies of tiles past the last one (the key loop issues
+  // the copies of tile t+PF without checking it against ntiles, which would cost a branch
+  // per copy) read zeros or, where their 32-bit offset wraps, bytes inside the buffer; the
+  // stages they fill are never read.  The offsets of the tiles that are read stay below
+  // 2^32: the validation keeps Lk*D below 2^31, and D (128 or 256) divides 2^31 by a
+  // multiple of 32 keys, so ntiles*TILE*2 <= 2^32.
   // (64-bit: ntiles*TILE*2 reaches 2^32 at the longest key sequences; the K bytes stay
   // below it)
   const uint32_t kv_lim = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       min(static_cast<uint64_t>(Lk - kbeg) * D * 2, static_cast<uint64_t>(ntiles) * TILE * 2)));
-  // K and V base addresses of this head as wave-uniform 64-bit values (scalar registers),
-  // so that the per-tile descriptors are scalar arithmetic.
-  auto uniform64 = [](const void* ptr) {
-    const uint64_t a = reinterpret_cast<uintptr_t>(ptr);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-  };
-  const uint64_t kb = uniform64(kh), vb = uniform64(vh);
+  const i32x4 krs = make_rsrc(kh, kv_lim), vrs = make_rsrc(vh, kv_lim);
   // Copy j (0 <= j < 2*LOADS) of this thread's share of tile t, into stage st: K copy
-  // round j/2 for even j, V round j/2 for odd j.  Branch-free: the round's first byte,
-  // off = t*TILE*2 + row offset, moves the descriptor's base (scalar arithmetic), and its
-  // size is what is left of the workgroup's bytes past it, clamped at 0, so rows past them
-  // (past Lk in a partial last tile, or a tile t past the last one) read as zeros and touch
-  // no memory.
+  // round j/2 for even j, V round j/2 for odd j.  Per copy: the LDS destination into M0,
+  // one vector add for the byte offset, the copy.
   auto issue_copy = [&](int t, int st, int j) {
     // (laundered: the destinations are added here, not kept per stage in scalar registers)
     uint32_t ks = lds_base + static_cast<uint32_t>(st * 2 * TILE);
@@ -397,20 +392,11 @@ void attn_fwd_kernel(Params p) {
     const bool isv = j & 1;
     const int i = j >> 1;
     const uint32_t dst = (isv ? ks + NSTAGE * 2 * TILE : ks) + (i * THREADS + wave * 64) * 16;
-    // (64-bit, clamped: the tiles past the last one may lie past 2^32 bytes)
-    const uint32_t off = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-        min(static_cast<uint64_t>(t) * TILE * 2 + i * ROWS_PER_LOAD * D * 2,
-            static_cast<uint64_t>(kv_lim))));
-    const uint64_t base = isv ? vb : kb;
-    uint32_t lo, hi, n;
-    asm("s_add_u32 %0, %3, %5\n\ts_addc_u32 %1, %4, 0\n\ts_sub_u32 %2, %6, %5\n\t"
-        "s_cselect_b32 %2, 0, %2"
-        : "=&s"(lo), "=&s"(hi), "=&s"(n)
-        : "s"(static_cast<uint32_t>(base)), "s"(static_cast<uint32_t>(base >> 32)), "s"(off),
-          "s"(kv_lim)
-        : "scc");
-    const i32x4 r = {static_cast<int>(lo), static_cast<int>(hi), static_cast<int>(n), 0x00020000};
-    lds_dma16(r, isv ? vv : vk[i & 1], dst);
+    // (laundered: a scalar sum added once per copy, so that the per-lane offsets of the
+    // rounds are not precomputed and held in vector registers)
+    uint32_t off = static_cast<uint32_t>(t) * (TILE * 2) + i * ROWS_PER_LOAD * D * 2;
+    asm volatile("" : "+s"(off));
+    lds_dma16(isv ? vrs : krs, off + (isv ? vv : vk[i & 1]), dst);
   };
   auto issue_tile = [&](int t, int st) {
 #pragma unroll
