@@ -220,6 +220,19 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t voffset, uint32_t
                : "memory");
 }
 
+// The key loop's copy: M0 <- wlds + dc (this wavefront's LDS slot plus a constant), the byte
+// offset <- soff + voff, then the copy; the vector add between the M0 write and the copy is
+// the wait state the copy needs after M0 is written.  Three instructions.
+__device__ __forceinline__ void lds_dma16_loop(i32x4 rsrc, uint32_t soff, uint32_t voff,
+                                               uint32_t wlds, uint32_t dc) {
+  uint32_t tmp;
+  asm volatile(
+      "s_add_u32 m0, %1, %2\n\tv_add_u32 %0, %3, %4\n\tbuffer_load_dwordx4 %0, %5, 0 offen lds"
+      : "=&v"(tmp)
+      : "s"(wlds), "i"(dc), "s"(soff), "v"(voff), "s"(rsrc)
+      : "memory", "scc");
+}
+
 // f(std::integral_constant<int, I>{}, t + I - I0) for I = I0 .. N-1 in order while
 // t + I - I0 < n; the first t not done.
 template <int I, int N, typename F>
@@ -385,18 +398,13 @@ void attn_fwd_kernel(Params p) {
   // Copy j (0 <= j < 2*LOADS) of this thread's share of tile t, into stage st: K copy
   // round j/2 for even j, V round j/2 for odd j.  Per copy: the LDS destination into M0,
   // one vector add for the byte offset, the copy.
+  const uint32_t wlds = __builtin_amdgcn_readfirstlane(lds_base + wave * 64 * 16);
   auto issue_copy = [&](int t, int st, int j) {
-    // (laundered: the destinations are added here, not kept per stage in scalar registers)
-    uint32_t ks = lds_base + static_cast<uint32_t>(st * 2 * TILE);
-    asm volatile("" : "+s"(ks));
     const bool isv = j & 1;
     const int i = j >> 1;
-    const uint32_t dst = (isv ? ks + NSTAGE * 2 * TILE : ks) + (i * THREADS + wave * 64) * 16;
-    // (laundered: a scalar sum added once per copy, so that the per-lane offsets of the
-    // rounds are not precomputed and held in vector registers)
-    uint32_t off = static_cast<uint32_t>(t) * (TILE * 2) + i * ROWS_PER_LOAD * D * 2;
-    asm volatile("" : "+s"(off));
-    lds_dma16(isv ? vrs : krs, off + (isv ? vv : vk[i & 1]), dst);
+    const uint32_t dc = (st + (isv ? NSTAGE : 0)) * 2 * TILE + i * THREADS * 16;
+    const uint32_t off = static_cast<uint32_t>(t) * (TILE * 2) + i * ROWS_PER_LOAD * D * 2;
+    lds_dma16_loop(isv ? vrs : krs, off, isv ? vv : vk[i & 1], wlds, dc);
   };
   auto issue_tile = [&](int t, int st) {
 #pragma unroll
