@@ -580,7 +580,7 @@ void attn_fwd_kernel(Params p) {
     // exp2(c*score - m) is exactly 0.  Accumulator register r of this lane holds key
     // kbeg + t*BN + 8*(r/4) + 4*hi + r%4 of query row qrow0 + 32*qb + l%32.  Only tiles
     // past the wave's common limit get here (the last tile, the diagonal band).
-    if (t * BN + BN - 1 > wave_lim) {
+    if (__builtin_expect(t * BN + BN - 1 > wave_lim, 0)) {
       // (t laundered: the per-register compares must not be hoisted out of the loop as
       // 16 loop-invariant lane masks held in scalar registers; the lane index recomputed
       // here rather than kept live across the loop)
@@ -682,7 +682,7 @@ void attn_fwd_kernel(Params p) {
       grown[qb] = __builtin_amdgcn_ballot_w64(lt[qb] > kGrowth<T>) != 0;
       any |= grown[qb];
     }
-    if (!any) return;
+    if (__builtin_expect(!any, 1)) return;
     u32x4 kf2[3];
     kf2[0] = kfrag(ksp, 0);
     kf2[1] = kfrag(ksp, 1);
@@ -729,11 +729,12 @@ void attn_fwd_kernel(Params p) {
   // into the stages of tiles t-3 and t-2; between barriers a wave is at most one iteration
   // ahead of another, and the stages one iteration reads (t, t-1) are never the ones the
   // other copies into.
-  auto sync_point = [&](int t) {
+  auto sync_point = [&]() {
     if constexpr (NSTAGE == 4 && PF == 2) {
       WAIT_VMCNT(NCOPY);  // this thread's copies of tile t+1 (those of t+2 may fly)
     } else {
-      if (t + 1 < ntiles) WAIT_VMCNT(0);  // this thread's copies of the tiles to come
+      WAIT_VMCNT(0);  // this thread's copies of the tiles to come (after the last tile:
+                      // those of the tiles past it)
     }
     // A bare s_barrier: every LDS read of this iteration has been waited for by the MFMA
     // that consumed it.
@@ -801,9 +802,10 @@ void attn_fwd_kernel(Params p) {
         if (h >= EXP0)
           exp_slice(sacc, NELEM * (h - EXP0) / (H - EXP0), NELEM * (h - EXP0 + 1) / (H - EXP0));
         // (six stages: odd iterations only; the stage parity is the iteration's parity)
-        if (h == H - 1 && (NSTAGE == 4 || ST % 2 == 1)) sync_point(t);
-        if (h == H - 1 && t + 1 < ntiles) {
-          // first two K fragments of tile t+1 (landed at the sync point)
+        if (h == H - 1 && (NSTAGE == 4 || ST % 2 == 1)) sync_point();
+        if (h == H - 1) {
+          // first two K fragments of tile t+1 (landed at the sync point; after the last
+          // tile an unused stage: reading it is harmless, a branch around it is not)
           kf[0] = kfrag(kstage((ST + 1) % NSTAGE), 0);
           kf[1] = kfrag(kstage((ST + 1) % NSTAGE), 1);
         }
