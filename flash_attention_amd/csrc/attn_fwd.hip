@@ -43,6 +43,7 @@
 // key loop.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <type_traits>
@@ -80,6 +81,13 @@ struct Params {
   int split_len;  // keys per split, a multiple of the key tile (split s: [s*len, (s+1)*len))
   int diag;       // row i sees key j only if j <= i + diag (Lk - Lq if causal, else Lk)
   int causal;     // heaviest query tiles first (their key range is the longest)
+  // Causal dispatch order when each head's rows fill whole query tiles (tiles_per_head
+  // tiles per head): the tiles of qperm_heads consecutive heads are dealt position-major,
+  // the last position of each of those heads first, then the one before it, and so on, so
+  // that the workgroups running at once on an XCD see nearly the same key range (and
+  // stream it through that XCD's L2 together).  qperm_heads <= 1: plain descending order.
+  int qperm_heads;
+  int tiles_per_head;
   // Query position of row r: r % lq_head.  The host passes the G query heads that share a
   // key/value head as one block of G*Lq rows (Hq = Hkv, G = 1 here), so a row's position
   // in its own head is its index modulo the per-head length; floor(r / lq_head) =
@@ -319,7 +327,20 @@ void attn_fwd_kernel(Params p) {
   int qtile = __builtin_amdgcn_readfirstlane(tile_id % p.n_qtiles);
   // causal: the last query tiles see the most keys; dispatching them first keeps the
   // light tiles for the end of the grid
-  if (p.causal) qtile = p.n_qtiles - 1 - qtile;
+  if (p.causal) {
+    if (p.qperm_heads > 1) {
+      // chunk c of H heads (fewer in a last partial chunk): position rank r of head h at
+      // index r*hc + h, positions from the last one down
+      const int tph = p.tiles_per_head, H = p.qperm_heads;
+      const int c = __builtin_amdgcn_readfirstlane(qtile / (H * tph));
+      const int j = qtile - c * (H * tph);
+      const int hc = min(H, p.n_qtiles / tph - c * H);
+      const int r = __builtin_amdgcn_readfirstlane(j / hc);
+      qtile = (c * H + (j - r * hc)) * tph + (tph - 1 - r);
+    } else {
+      qtile = p.n_qtiles - 1 - qtile;
+    }
+  }
   // (row blocks as the host passes them: with each key/value group as one block, p.Hq =
   // Hkv and p.G = 1)
   const int bh = __builtin_amdgcn_readfirstlane(tile_id / p.n_qtiles);  // b*p.Hq + hq
@@ -1000,6 +1021,17 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
   const bool causal = (flags & ATTN_CAUSAL) != 0;
   prm.diag = static_cast<int>(causal ? Lk - Lq : Lk);
   prm.causal = causal ? 1 : 0;
+  // Causal dispatch order: heads whose query rows fill whole tiles are dealt position-major
+  // in chunks of as many heads as one XCD's share of the grid holds (workgroups go to the
+  // 8 XCDs in contiguous ranges).
+  prm.qperm_heads = 1;
+  prm.tiles_per_head = 1;
+  if (causal && Lq > 0 && Lq % block_m == 0) {
+    const int64_t T = Lq / block_m;
+    const int64_t per_xcd = (static_cast<int64_t>(prm.n_work) + 7) / 8 / nsplit;
+    prm.qperm_heads = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(G, per_xcd / T)));
+    prm.tiles_per_head = static_cast<int>(T);
+  }
   prm.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
   // scale == 0: every weight is 1.  A positive c this small gives c*score below 2^-60 for
   // any finite fp16/bf16 dot product, so exp2 rounds to exactly 1 and the LSE term c*m

@@ -51,6 +51,26 @@ def test_causal_parity(case):
     parity(q, k, v, scale_of(D), dt, what="causal " + str(case), causal=True)
 
 
+# Shapes whose heads fill whole 256-row query tiles and whose grid gives each XCD several
+# heads: the causal launch then deals each XCD's tiles position-major over chunks of
+# heads (chunk sizes 4, 4 with a partial last chunk of 2, 4 with two key splits, 3).
+ORDER = [  # B, Hq, Hkv, Lq, Lk, D, dtype, nsplit, seed
+    (1, 32, 2, 1024, 1024, 256, "f16", 1, 9501), (5, 6, 1, 256, 300, 128, "bf16", 1, 9502),
+    (2, 16, 2, 512, 512, 128, "f16", 2, 9503), (1, 24, 2, 768, 800, 256, "bf16", 1, 9504),
+]
+
+
+@pytest.mark.parametrize("case", ORDER, ids=["B%d_H%d_%d_L%dx%d_D%d_%s_n%d_s%d" % c
+                                             for c in ORDER])
+def test_causal_dispatch_order(case):
+    """Every query tile is computed once whatever order the workgroups take them in."""
+    B, Hq, Hkv, Lq, Lk, D, dt, nsplit, seed = case
+    _announce("causal dispatch order " + str(case))
+    q, k, v = attn_inputs.make_qkv(B, Hq, Hkv, Lq, Lk, D, dt, seed=seed)
+    parity(q, k, v, scale_of(D), dt, what="causal order " + str(case), causal=True,
+           nsplit=nsplit)
+
+
 @pytest.mark.parametrize("D,dt", [(128, "f16"), (256, "bf16")])
 def test_causal_first_row_is_exact(D, dt):
     """Lq = Lk: row 0 sees key 0 alone, so its weight is exactly 1 and O equals V_0 bit
