@@ -24,7 +24,11 @@
  * O is written in the input type (round to nearest even); LSE in fp32.  The scores
  * scale * q.k are formed in fp32 and must be finite there: with fp16 inputs that holds for
  * any |scale| below about 1e26 / D; with bf16 inputs (whose range is fp32's) it is the
- * caller's data that must keep q.k within fp32.
+ * caller's data that must keep q.k within fp32.  The output accumulates unnormalised
+ * weights in fp32, each 32-key tile's weights of a row summing to at most 2^16 (fp16
+ * inputs) or 2^25 (bf16 inputs) against the row's softmax reference: with bf16 inputs the
+ * values of V must stay below 2^103 / ceil(Lk / 32) in magnitude (about 1e28 at 16K keys,
+ * 4e25 at the longest accepted key sequence); fp16 values never reach that bound.
  *
  * Causal masking (attn_fwd_ex, flag ATTN_CAUSAL).  Query row i sees key j
  * only if j <= i + (Lk - Lq): the diagonal is aligned to the end of both

@@ -300,6 +300,33 @@ def test_reference_growth_last_tile_and_repeated():
     parity(q, k, v, scale_of(D), "f16", what="growth repeated")
 
 
+@pytest.mark.parametrize("D,dt,k,growth", [(128, "bf16", 60, False), (256, "bf16", 80, True),
+                                          (256, "f16", 8, True)])
+def test_values_scaled_by_power_of_two(D, dt, k, growth):
+    """V times 2^k gives O times 2^k bit for bit (where O is a normal number of its type) and
+    the same LSE: the weights and the accumulation are linear in V, and scaling by a power
+    of two rounds nothing while the fp32 accumulator stays in range (bf16 values up to
+    ~2^83 here, far above fp16's range, with rescales mid-sweep in the growth cases)."""
+    _announce("V scaled by 2^%d D=%d %s growth=%s" % (k, D, dt, growth))
+    if growth:
+        q, k_, v = _growing_scores(D, dt, 900, [(130, 200.0), (480, 350.0)], seed=31)
+    else:
+        q, k_, v = attn_inputs.make_qkv(1, 4, 2, 300, 700, D, dt, seed=31)
+    if dt == "f16":
+        v = (v.double().clamp(-4, 4)).to(v.dtype)  # 4 * 2^8 stays inside fp16
+    big = (v.double() * 2.0 ** k).to(v.dtype)
+    assert torch.equal(big.double(), v.double() * 2.0 ** k)  # the scaling itself is exact
+    o1, l1 = gpu_fwd(q, k_, v, scale_of(D))
+    o2, l2 = gpu_fwd(q, k_, big, scale_of(D))
+    # an unscaled output below the output type's smallest normal (fp16: 2^-14) is rounded to
+    # the subnormal spacing (2^-24), its scaled twin to full precision
+    a, b = o1.double(), o2.double() / 2.0 ** k
+    normal = a.abs() >= (2.0 ** -14 if dt == "f16" else 2.0 ** -126)
+    assert torch.equal(b[normal], a[normal])
+    assert bool(((b - a)[~normal].abs() <= 2.0 ** -25).all())
+    assert torch.equal(l1, l2)
+
+
 @pytest.mark.parametrize("D,dt", [(256, "f16"), (128, "bf16")])
 def test_reference_growth_in_one_block_only(D, dt):
     """Growth confined to one 32-row query block: every query row is made orthogonal to a
