@@ -427,6 +427,33 @@ void attn_fwd_kernel(Params p) {
     const uint32_t off = static_cast<uint32_t>(t) * (TILE * 2) + i * ROWS_PER_LOAD * D * 2;
     lds_dma16_loop(isv ? vrs : krs, off, isv ? vv : vk[i & 1], wlds, dc);
   };
+  // Six stages (the HD=128 wide shape, two wavefronts per SIMD): inside the key loop only
+  // the first half of the wavefronts copies (waves w and w + WAVES/2 share a SIMD), so that
+  // the second half can meet the barrier half an iteration later than the first (at the
+  // sync point below); elsewhere every thread copies, as in the prologue.
+  constexpr bool PP = NSTAGE == 6;
+  constexpr int CT = PP ? THREADS / 2 : THREADS;  // threads that copy inside the key loop
+  constexpr int LOADS_L = BN * CPR / CT;           // their copies per tile, K (or V)
+  constexpr int ROWS_L = CT / CPR;
+  static_assert(LOADS_L >= 1 && BN * CPR % CT == 0, "whole copy rounds per tile");
+  uint32_t vkL[2], vvL;
+  {
+    const int pos0 = (wave * 64 + lane) % CT;
+    const int r0 = pos0 / CPR, c0 = pos0 % CPR;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      vkL[par] = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_k(par * ROWS_L + r0)) * 16);
+    vvL = static_cast<uint32_t>(r0 * D * 2 + (c0 ^ swz_v(r0)) * 16);
+  }
+  // Copy j (0 <= j < 2*LOADS_L) of a copying thread's share of tile t, as issue_copy with
+  // CT threads.
+  auto issue_copy_loop = [&](int t, int st, int j) {
+    const bool isv = j & 1;
+    const int i = j >> 1;
+    const uint32_t dc = (st + (isv ? NSTAGE : 0)) * 2 * TILE + i * CT * 16;
+    const uint32_t off = static_cast<uint32_t>(t) * (TILE * 2) + i * ROWS_L * D * 2;
+    lds_dma16_loop(isv ? vrs : krs, off, isv ? vvL : vkL[i & 1], wlds, dc);
+  };
   auto issue_tile = [&](int t, int st) {
 #pragma unroll
     for (int j = 0; j < 2 * LOADS; ++j) issue_copy(t, st, j);
@@ -738,21 +765,26 @@ void attn_fwd_kernel(Params p) {
     }
   };
 
-  constexpr int NCOPY = 2 * LOADS;  // copies per thread and tile
+  constexpr int NCOPY = 2 * LOADS;      // copies per thread and tile (prologue)
+  constexpr int NCOPY_L = 2 * LOADS_L;  // the same inside the key loop, per copying thread
 
   // Synchronisation point at the end of iteration t.  Four stages (every iteration): tile
   // t+1 has landed everywhere (copied in iteration t, or t-1 with PF = 2, whose copies of
   // tile t+2 may still be in flight: a wave waits until at most its own NCOPY newest copies
   // are), and every wave is done with tile t-1, so the next iteration may read tile t+1 and
-  // copy tile t+1+PF into the stage of tile t+1+PF-4.  Six stages (odd t only): tiles t+1
-  // and t+2 (copied in iterations t-1 and t) have landed everywhere and every wave is done
-  // with iteration t, so the next two iterations may read them and copy tiles t+3 and t+4
-  // into the stages of tiles t-3 and t-2; between barriers a wave is at most one iteration
-  // ahead of another, and the stages one iteration reads (t, t-1) are never the ones the
-  // other copies into.
+  // copy tile t+1+PF into the stage of tile t+1+PF-4.  Six stages (odd t only; only the
+  // first half of the wavefronts copies, and the second half meets this barrier after its
+  // S^T phase of iteration t, half an iteration behind, so that the two wavefronts of a SIMD
+  // keep one's S^T MFMAs beside the other's exponentials): the copying wavefronts have
+  // waited for their copies of tiles t+1 and t+2 (issued in iterations t-1 and t), so those
+  // tiles have landed everywhere; every wave has finished iteration t-1 (the second half
+  // still has the P.V product of tile t-1 to do, reading V(t-1) only).  Until the next
+  // barrier the first half runs iterations t+1, t+2 and copies tiles t+3 and t+4 into the
+  // stages of tiles t-3 and t-2, which no wave reads any more; the second half reads tiles
+  // t-1 .. t+2 only, all landed.
   auto sync_point = [&]() {
     if constexpr (NSTAGE == 4 && PF == 2) {
-      WAIT_VMCNT(NCOPY);  // this thread's copies of tile t+1 (those of t+2 may fly)
+      WAIT_VMCNT(NCOPY_L);  // this thread's copies of tile t+1 (those of t+2 may fly)
     } else {
       WAIT_VMCNT(0);  // this thread's copies of the tiles to come (after the last tile:
                       // those of the tiles past it)
@@ -767,16 +799,17 @@ void attn_fwd_kernel(Params p) {
   u32x4 kf[3];
   constexpr int NPAIR = NELEM / 2;  // packed weight pairs per lane and tile
   // ST = t % NSTAGE, a compile-time constant: the key loop is unrolled by NSTAGE.
-  auto iteration = [&](auto pv_tag, auto st_tag, int t, f32x16 (&sacc)[QB]) {
+  auto iteration = [&](auto pv_tag, auto st_tag, auto gb_tag, int t, f32x16 (&sacc)[QB]) {
     constexpr bool PV = decltype(pv_tag)::value;
     constexpr int ST = decltype(st_tag)::value;
+    constexpr bool GB = decltype(gb_tag)::value;  // the second half of the wavefronts (PP)
     constexpr int VST = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
     u32x4 vf[3];
     // S^T(t); under its MFMAs the weights of tile t-1 are packed, and the copies of tile
     // t+PF issued into the stage of tile t+PF-NSTAGE (t-3, or t-4 with six stages: free,
     // every wave is past the iteration that last read it), copy j after MFMA j*W/NCOPY
     constexpr int W = QB * KS;  // S^T windows
-    static_assert(W % NCOPY == 0, "whole S^T windows per copy");
+    static_assert(W % NCOPY_L == 0, "whole S^T windows per copy");
     qk(kstage(ST), sacc, kf,
        [&]() {
          if constexpr (PV) {
@@ -786,13 +819,19 @@ void attn_fwd_kernel(Params p) {
        },
        [&](int w) {
          if constexpr (PV) pack_slice(NPAIR * w / W, NPAIR * (w + 1) / W);
-         if (w % (W / NCOPY) == 0) issue_copy(t + PF, (ST + PF) % NSTAGE, w / (W / NCOPY));
+         if constexpr (!GB) {
+           if (w % (W / NCOPY_L) == 0)
+             issue_copy_loop(t + PF, (ST + PF) % NSTAGE, w / (W / NCOPY_L));
+         }
        });
     if constexpr (PV) {
       rescale_if_grown(t - 1, kstage(VST), kstage(ST), sacc);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
     }
+    // the second half of the wavefronts meets the barrier of odd iterations here, after its
+    // S^T phase (it has no copies of its own in flight)
+    if constexpr (GB && ST % 2 == 1) __builtin_amdgcn_s_barrier();
     // Each P.V step is QB sub-steps: one MFMA (query block qb), then a slice of VALU or
     // copy work that issues while that MFMA runs.  A wave issues in order, so work placed
     // after an MFMA overlaps it only until the next MFMA: one sub-step per MFMA gives
@@ -823,7 +862,7 @@ void attn_fwd_kernel(Params p) {
         if (h >= EXP0)
           exp_slice(sacc, NELEM * (h - EXP0) / (H - EXP0), NELEM * (h - EXP0 + 1) / (H - EXP0));
         // (six stages: odd iterations only; the stage parity is the iteration's parity)
-        if (h == H - 1 && (NSTAGE == 4 || ST % 2 == 1)) sync_point();
+        if (h == H - 1 && (NSTAGE == 4 || (ST % 2 == 1 && !GB))) sync_point();
         if (h == H - 1) {
           // first two K fragments of tile t+1 (landed at the sync point; after the last
           // tile an unused stage: reading it is harmless, a branch around it is not)
@@ -866,23 +905,33 @@ void attn_fwd_kernel(Params p) {
     __syncthreads();
     kf[0] = kfrag(kstage(0), 0);
     kf[1] = kfrag(kstage(0), 1);
-    iteration(std::false_type{}, std::integral_constant<int, 0>{}, 0, sacc);
-    int t = 1;
-    // unrolled by NSTAGE: iteration t runs with stage t % NSTAGE as a compile-time constant
-    while (t < ntiles) {
-#define ATTN_ITER(J)                                                                   \
-  iteration(std::true_type{}, std::integral_constant<int, (1 + (J)) % NSTAGE>{}, t, sacc); \
+    // unrolled by NSTAGE: iteration t runs with stage t % NSTAGE as a compile-time constant;
+    // one copy of the loop per half of the wavefronts where they differ (PP)
+#define ATTN_ITER(J, GBT)                                                                 \
+  iteration(std::true_type{}, std::integral_constant<int, (1 + (J)) % NSTAGE>{}, GBT{}, t, \
+            sacc);                                                                        \
   if (++t >= ntiles) break;
-      ATTN_ITER(0)
-      ATTN_ITER(1)
-      ATTN_ITER(2)
-      ATTN_ITER(3)
-      if constexpr (NSTAGE == 6) {
-        ATTN_ITER(4)
-        ATTN_ITER(5)
-      }
+#define ATTN_KEY_LOOP(GBT)                                                                \
+  {                                                                                       \
+    iteration(std::false_type{}, std::integral_constant<int, 0>{}, GBT{}, 0, sacc);      \
+    int t = 1;                                                                            \
+    while (t < ntiles) {                                                                  \
+      ATTN_ITER(0, GBT)                                                                   \
+      ATTN_ITER(1, GBT)                                                                   \
+      ATTN_ITER(2, GBT)                                                                   \
+      ATTN_ITER(3, GBT)                                                                   \
+      if constexpr (NSTAGE == 6) {                                                        \
+        ATTN_ITER(4, GBT)                                                                 \
+        ATTN_ITER(5, GBT)                                                                 \
+      }                                                                                   \
+    }                                                                                     \
+  }
+    // (written out twice rather than as a lambda: the backend mishandles the key loop inside
+    // a lambda)
+    if (PP && wave >= WAVES / 2) ATTN_KEY_LOOP(std::true_type)
+    else ATTN_KEY_LOOP(std::false_type)
+#undef ATTN_KEY_LOOP
 #undef ATTN_ITER
-    }
     drain(ntiles - 1, sacc);
     // the last iteration copied (zeros) for a tile past the end: let it land before the
     // workgroup's LDS is released
