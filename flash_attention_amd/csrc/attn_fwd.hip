@@ -429,8 +429,8 @@ void attn_fwd_kernel(Params p) {
   };
   // Six stages (the HD=128 wide shape, two wavefronts per SIMD): inside the key loop only
   // the first half of the wavefronts copies (waves w and w + WAVES/2 share a SIMD), so that
-  // the second half can meet the barrier half an iteration later than the first (at the
-  // sync point below); elsewhere every thread copies, as in the prologue.
+  // the second half can meet the barrier at another point of its iteration than the first
+  // (see the sync point below); elsewhere every thread copies, as in the prologue.
   constexpr bool PP = NSTAGE == 6;
   constexpr int CT = PP ? THREADS / 2 : THREADS;  // threads that copy inside the key loop
   constexpr int LOADS_L = BN * CPR / CT;           // their copies per tile, K (or V)
@@ -773,15 +773,15 @@ void attn_fwd_kernel(Params p) {
   // tile t+2 may still be in flight: a wave waits until at most its own NCOPY newest copies
   // are), and every wave is done with tile t-1, so the next iteration may read tile t+1 and
   // copy tile t+1+PF into the stage of tile t+1+PF-4.  Six stages (odd t only; only the
-  // first half of the wavefronts copies, and the second half meets this barrier after its
-  // S^T phase of iteration t, half an iteration behind, so that the two wavefronts of a SIMD
-  // keep one's S^T MFMAs beside the other's exponentials): the copying wavefronts have
-  // waited for their copies of tiles t+1 and t+2 (issued in iterations t-1 and t), so those
-  // tiles have landed everywhere; every wave has finished iteration t-1 (the second half
-  // still has the P.V product of tile t-1 to do, reading V(t-1) only).  Until the next
-  // barrier the first half runs iterations t+1, t+2 and copies tiles t+3 and t+4 into the
-  // stages of tiles t-3 and t-2, which no wave reads any more; the second half reads tiles
-  // t-1 .. t+2 only, all landed.
+  // first half of the wavefronts copies, and the second half meets this barrier in the
+  // middle of its S^T phase of iteration t, about three quarters of an iteration behind, so
+  // that the two wavefronts of a SIMD do not fall into the same phase): the copying
+  // wavefronts have waited for their copies of tiles t+1 and t+2 (issued in iterations t-1
+  // and t), so those tiles have landed everywhere; every wave has finished iteration t-1.
+  // Until the next barrier the first half runs iterations t+1, t+2 and copies tiles t+3 and
+  // t+4 into the stages of tiles t-3 and t-2, which no wave reads any more; the second half
+  // reads tiles t-1 .. t+2 only (the rest of iteration t, iteration t+1 and half of the
+  // S^T phase of iteration t+2), all landed.
   auto sync_point = [&]() {
     if constexpr (NSTAGE == 4 && PF == 2) {
       WAIT_VMCNT(NCOPY_L);  // this thread's copies of tile t+1 (those of t+2 may fly)
@@ -818,6 +818,11 @@ void attn_fwd_kernel(Params p) {
          }
        },
        [&](int w) {
+         // the second half of the wavefronts meets the barrier of odd iterations here, in
+         // the middle of its S^T phase (it has no copies of its own in flight)
+         if constexpr (GB && ST % 2 == 1) {
+           if (w == W / 2) __builtin_amdgcn_s_barrier();
+         }
          if constexpr (PV) pack_slice(NPAIR * w / W, NPAIR * (w + 1) / W);
          if constexpr (!GB) {
            if (w % (W / NCOPY_L) == 0)
@@ -829,9 +834,6 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) l[qb] += lt[qb];
     }
-    // the second half of the wavefronts meets the barrier of odd iterations here, after its
-    // S^T phase (it has no copies of its own in flight)
-    if constexpr (GB && ST % 2 == 1) __builtin_amdgcn_s_barrier();
     // Each P.V step is QB sub-steps: one MFMA (query block qb), then a slice of VALU or
     // copy work that issues while that MFMA runs.  A wave issues in order, so work placed
     // after an MFMA overlaps it only until the next MFMA: one sub-step per MFMA gives
