@@ -22,6 +22,10 @@ of its known byte count to what the counter reads for it calibrates the counter,
 kernel's reading is scaled by that ratio.  Counter passes run under a hard kill timeout
 so that a refused counter request cannot leave a hung profiler behind.
 
+With --sq it instead runs three passes of SQ (sequencer) counters per workload (cycles,
+matrix-core busy cycles, wait and issue counters, instruction counts) and writes one
+summary of where a launch's cycles go and at what average clock it ran.
+
 Prints a markdown summary (also written to --md, or to <md-dir>/<kernel>__<workload>.md)
 and, with --traffic-json, records the calibrated bytes per launch under the workload's name
 together with the hash of the kernel sources, so that bench.py reports them only while the
@@ -197,6 +201,9 @@ def main():
                     help="timed launches of the trace pass (bench.py's default)")
     ap.add_argument("--trace-warmup", type=int, default=5)
     ap.add_argument("--kill-after", type=int, default=90)
+    ap.add_argument("--sq", action="store_true",
+                    help="SQ counter passes instead (--workload may list several, comma-"
+                         "separated); the summary goes to --md")
     ap.add_argument("--index", default=None,
                     help="only write a table of every workload in this --traffic-json file "
                          "(to --md) and exit")
@@ -204,6 +211,8 @@ def main():
     # (paths inside the repository are shown relative to its root)
     a.command = "python -m flash_attention_amd.rocprof_harness " + " ".join(
         os.path.relpath(x, ROOT) if x.startswith(ROOT + os.sep) else x for x in sys.argv[1:])
+    if a.sq:
+        return sq_profile(a.workload.split(","), os.path.abspath(a.outdir), a)
     if a.index:
         text = index_table(a.index, a.command)
         print(text)
@@ -359,6 +368,138 @@ def index_table(traffic_json, command):
             s["fetch_bytes_per_launch"] / s["algorithmic_read_bytes"],
             s["write_bytes_per_launch"] / 1e6))
     out.append("")
+    return "\n".join(out)
+
+
+# SQ counters of the three --sq passes (at most 8 SQ counters per pass).
+SQ_PASSES = [
+    ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+     "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES"],
+    ["SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_INST_LEVEL_LDS", "SQ_LDS_IDX_ACTIVE",
+     "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL", "SQ_IFETCH", "SQ_ACTIVE_INST_VMEM"],
+    ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_SCA",
+     "SQ_ACTIVE_INST_MISC", "SQ_INSTS_VMEM", "SQ_IFETCH_LEVEL"],
+]
+MFMA_FLOP = 2 * 32 * 32 * 16  # one v_mfma_f32_32x32x16_{f16,bf16}
+
+
+def gpu_agent(outdir, name):
+    """(shader engines, SIMDs) of the GPU in a pass's agent table."""
+    for r in _rows(os.path.join(outdir, name, "**", "*agent_info.csv")):
+        if r.get("Agent_Type") == "GPU":
+            return int(r["Num_Shader_Banks"]), int(r["Simd_Count"])
+    raise RuntimeError("%s: no GPU agent in the agent table" % name)
+
+
+def sq_launches(outdir, name):
+    """[(counter values, duration ns)] of the attention launches of one pass."""
+    res = {}
+    for r in _rows(os.path.join(outdir, name, "**", "*counter_collection.csv")):
+        if KERNEL_TAG not in r["Kernel_Name"]:
+            continue
+        vals, _ = res.setdefault(int(r["Dispatch_Id"]), ({}, None))
+        vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        res[int(r["Dispatch_Id"])] = (vals, int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return [res[d] for d in sorted(res)]
+
+
+def sq_figures(launches, engines, simds, flops):
+    """Medians of every counter over the launches, and what follows from them: SQ cycle
+    counters are summed over the shader engines, the matrix-core busy cycles over the
+    SIMDs."""
+    names = sorted({k for v, _ in launches for k in v})
+    med = {k: statistics.median(v[k] for v, _ in launches if k in v) for k in names}
+    cyc = med["SQ_BUSY_CYCLES"] / engines
+    clocks = [v["SQ_BUSY_CYCLES"] / engines / (ns * 1e-9) / 1e6
+              for v, ns in launches if "SQ_BUSY_CYCLES" in v and ns > 0]
+    fig = {
+        "mfma_per_algorithmic": med["SQ_INSTS_MFMA"] / (flops / MFMA_FLOP),
+        "valu_per_mfma": (med["SQ_INSTS_VALU"] - med["SQ_INSTS_MFMA"]) / med["SQ_INSTS_MFMA"],
+        "lds_per_mfma": med["SQ_INSTS_LDS"] / med["SQ_INSTS_MFMA"],
+        "cycles_per_mfma": med["SQ_VALU_MFMA_BUSY_CYCLES"] / med["SQ_INSTS_MFMA"],
+        "cycles_per_launch": cyc,
+        "mfma_busy_pct": 100 * med["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cyc,
+        "clock_mhz_min": min(clocks), "clock_mhz_max": max(clocks),
+        "wait_any_pct": 100 * med["SQ_WAIT_ANY"] / med["SQ_WAVE_CYCLES"],
+        "wait_inst_any_pct": 100 * med["SQ_WAIT_INST_ANY"] / med["SQ_WAVE_CYCLES"],
+        "active_valu_pct": 100 * med["SQ_ACTIVE_INST_VALU"] / med["SQ_WAVE_CYCLES"],
+    }
+    return med, fig
+
+
+def sq_profile(workloads, out, a):
+    """The three SQ passes over each workload, then one summary of them all."""
+    sys.path.insert(0, ROOT)
+    import attn_inputs  # noqa: E402  (shapes only; imports no GPU code)
+    import bench  # noqa: E402
+    cmds, sections = [], []
+    for wl in workloads:
+        w = attn_inputs.WORKLOADS[wl]
+        wout = os.path.join(out, wl)
+        os.makedirs(wout, exist_ok=True)
+        for i, ctrs in enumerate(SQ_PASSES, 1):
+            cmd = (["rocprofv3", "--pmc"] + ctrs + ["-f", "csv", "-d",
+                   os.path.join(wout, "sq%d" % i), "-o", "p", "--"] +
+                   _bench_cmd(wl, a.steps, 1, False))
+            if wl == workloads[0]:
+                cmds.append(cmd)
+            rc = _run(cmd, os.path.join(wout, "sq%d.log" % i), a.kill_after)
+            if rc not in (0, 139):
+                print("[harness] SQ pass %d failed (exit %d); stopping" % (i, rc), flush=True)
+                return rc
+        engines, simds = gpu_agent(wout, "sq1")
+        launches = []
+        for i in range(1, len(SQ_PASSES) + 1):
+            launches += sq_launches(wout, "sq%d" % i)
+        med, fig = sq_figures(launches, engines, simds, bench.flops_workload(w))
+        sections.append((wl, w, med, fig, engines, simds))
+    md = sq_markdown(a, cmds, sections, bench.kernel_source_hash())
+    print(md)
+    if a.md:
+        with open(a.md, "w") as f:
+            f.write(md)
+    return 0
+
+
+def sq_markdown(a, cmds, sections, sha):
+    def rel(c):
+        return " ".join("python3" if x == sys.executable else
+                        os.path.relpath(x, ROOT) if x.startswith(ROOT) else x for x in c)
+
+    out = ["# attn_fwd: issue and stall counters (SQ block), %s" %
+           ", ".join(wl for wl, *_ in sections), "",
+           "Made by (repository root on the MI355X box; every pass is a child process, run "
+           "from /tmp with TMPDIR=/tmp):", "", "    " + a.command, "",
+           "which runs, for each workload (here the first):", ""]
+    out += ["    " + rel(c) for c in cmds]
+    out += ["", "Kernel source hash: `%s`.  Values are medians over the attention launches of "
+            "the passes (1 warm-up + %d timed each).  SQ cycle counters are summed over the "
+            "GPU's shader engines, the matrix-core busy cycles over its SIMDs (both from the "
+            "profiler's agent table); a launch's duration comes from the same rows' "
+            "timestamps." % (sha, a.steps), ""]
+    for wl, w, med, fig, engines, simds in sections:
+        out += ["## %s (%s)" % (wl, w.describe()), "", "| counter | median per launch |",
+                "|---|---|"]
+        out += ["| `%s` | %.4g |" % (k, med[k]) for k in sorted(med)]
+        out += ["", "Derived (%d shader engines, %d SIMDs):" % (engines, simds), "",
+                "| figure | value |", "|---|---|",
+                "| MFMA instructions / (algorithmic flops / %d per v_mfma_f32_32x32x16) | %.4f |"
+                % (MFMA_FLOP, fig["mfma_per_algorithmic"]),
+                "| other VALU instructions per MFMA | %.2f |" % fig["valu_per_mfma"],
+                "| LDS instructions per MFMA | %.2f |" % fig["lds_per_mfma"],
+                "| matrix-core busy cycles per MFMA | %.2f |" % fig["cycles_per_mfma"],
+                "| cycles per launch (`SQ_BUSY_CYCLES` / shader engines) | %.4gM |"
+                % (fig["cycles_per_launch"] / 1e6),
+                "| matrix-core busy per SIMD (`SQ_VALU_MFMA_BUSY_CYCLES` / SIMDs / cycles per "
+                "launch) | %.1f %% |" % fig["mfma_busy_pct"],
+                "| average clock of the profiled launches (cycles / duration) | %.0f-%.0f MHz |"
+                % (fig["clock_mhz_min"], fig["clock_mhz_max"]),
+                "| wave time in dependency waits (`SQ_WAIT_ANY` / `SQ_WAVE_CYCLES`) | %.1f %% |"
+                % fig["wait_any_pct"],
+                "| wave time waiting to issue (`SQ_WAIT_INST_ANY` / `SQ_WAVE_CYCLES`) | %.1f %% |"
+                % fig["wait_inst_any_pct"],
+                "| wave time issuing VALU (`SQ_ACTIVE_INST_VALU` / `SQ_WAVE_CYCLES`) | %.1f %% |"
+                % fig["active_valu_pct"], ""]
     return "\n".join(out)
 
 

@@ -99,3 +99,45 @@ def test_kernel_stats_and_index(tmp_path):
     text = rh.index_table(str(p), "python -m x")
     assert "| w1 | abc | 100 | 7.0000 | 0.5 | 0.5000 | 1800 | 63.0 | 0.0000 | 600.0 (2.00) | 200.0 |" in text
     assert "| old |" not in text
+
+
+def _write_sq_pass(d, name, rows, engines=32, simds=1024):
+    """A --pmc pass directory: agent table and counter rows (dispatch, kernel, counter,
+    value, start, end)."""
+    base = os.path.join(d, name, "host")
+    os.makedirs(base, exist_ok=True)
+    with open(os.path.join(base, "p_agent_info.csv"), "w") as f:
+        f.write("Agent_Type,Num_Shader_Banks,Simd_Count\n")
+        f.write('"CPU",0,0\n"GPU",%d,%d\n' % (engines, simds))
+    with open(os.path.join(base, "p_counter_collection.csv"), "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,"
+                "End_Timestamp\n")
+        for r in rows:
+            f.write('%d,"%s","%s",%f,%d,%d\n' % r)
+
+
+def test_sq_figures(tmp_path):
+    """Cycles per launch are the busy cycles over the shader engines, matrix-core busy the
+    MFMA busy cycles over SIMDs and cycles, the clock cycles over duration; other kernels'
+    rows are ignored."""
+    d = str(tmp_path)
+    k = "_ZN12_GLOBAL__N_115attn_fwd_kernelILi256ELi0EDF16_Lb0EEEvNS_6ParamsE"
+    flops = 1000 * rh.MFMA_FLOP  # 1000 algorithmic MFMAs
+    rows = []
+    for disp, t0 in ((2, 0), (3, 10_000)):  # two launches of 2 us each
+        vals = {"SQ_BUSY_CYCLES": 32 * 3000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 2400.0,
+                "SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 250.0, "SQ_WAIT_INST_ANY": 100.0,
+                "SQ_ACTIVE_INST_VALU": 400.0, "SQ_INSTS_MFMA": 1000.0, "SQ_INSTS_VALU": 3000.0,
+                "SQ_INSTS_LDS": 750.0}
+        rows += [(disp, k, c, v, t0, t0 + 2000) for c, v in vals.items()]
+    rows.append((1, "copy_kernel", "SQ_BUSY_CYCLES", 1e9, 0, 10))
+    _write_sq_pass(d, "sq1", rows)
+    assert rh.gpu_agent(d, "sq1") == (32, 1024)
+    launches = rh.sq_launches(d, "sq1")
+    assert len(launches) == 2 and launches[0][1] == 2000
+    med, fig = rh.sq_figures(launches, 32, 1024, flops)
+    assert fig["cycles_per_launch"] == 3000.0
+    assert abs(fig["mfma_busy_pct"] - 80.0) < 1e-9
+    assert abs(fig["clock_mhz_min"] - 1500.0) < 1e-9  # 3000 cycles in 2 us
+    assert fig["mfma_per_algorithmic"] == 1.0 and fig["valu_per_mfma"] == 2.0
+    assert fig["lds_per_mfma"] == 0.75 and fig["wait_any_pct"] == 25.0
