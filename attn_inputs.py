@@ -89,6 +89,12 @@ WORKLOADS = {
                                k_mult=4.0, seed_base=10000),
     "gqa16k_d256_k8": Workload("gqa16k_d256_k8", 1, 32, 2, 16384, 16384, 256, "f16",
                                k_mult=8.0, seed_base=11000),
+    # Each head dimension's square case with the other 16-bit input type, so that all four
+    # kernels (HD 128/256 x fp16/bf16) have a timed workload.
+    "gqa16k_d256_bf16": Workload("gqa16k_d256_bf16", 1, 32, 2, 16384, 16384, 256, "bf16",
+                                 seed_base=12000),
+    "gqa8k_d128_f16": Workload("gqa8k_d128_f16", 1, 32, 8, 8192, 8192, 128, "f16",
+                               seed_base=13000),
 }
 HEADLINE = "gqa16k_d256"
 
